@@ -1,0 +1,287 @@
+"""Benchmark of the 4-bit weight-quantized matmul path on one MI355X.
+
+Metric: Q4 GEMV effective HBM GB/s (M=1) + MMQ prefill TOPS (M=512/2048).
+
+One timed step = one pass of the whole hot path over synthetic inputs already
+resident in HBM:
+  decode leg  -- one decoded token of a ~4B dense transformer at M = 1: the
+                 projection set q, k, v (2560 -> 4096/1024/1024), o
+                 (4096 -> 2560), gate, up (2560 -> 9216), down (9216 -> 2560)
+                 for each of 36 layers with distinct weights, replayed as one
+                 HIP graph, then the lm_head GEMV (2560 -> 151936) launched
+                 on its own between HIP events.  2.01 GB of packed weights per
+                 token, far above the 256 MB Infinity Cache.
+  prefill leg -- Q8_1 quantization of the activations followed by the MMQ
+                 GEMM for M = 2048 tokens on a ~9B-shaped layer pair
+                 (4096 -> 12288 and 12288 -> 4096, 1 % outliers at 20x) and for
+                 M = 512 (2560 -> 9216).
+value = algorithmic bytes of the decode leg / decode leg time (GB/s);
+the MMQ TOPS (2 M N K / kernel time) are reported under "mmq_prefill".
+Algorithmic bytes of a GEMV: packed weights N*K/2 + scales N*K/256*4 + x M*K*4
++ y M*N*4.  Packing (q4_pack) is setup and is not timed.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+I8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+LAYERS = 36
+
+
+def gemv_bytes(M, N, K):
+    return N * K // 2 + N * (K // 256) * 4 + M * K * 4 + M * N * 4
+
+
+def mmq_bytes(M, N, K):
+    return N * K // 2 + N * (K // 256) * 4 + M * K + M * (K // 32) * 4 + M * N * 4
+
+
+def q8_bytes(M, K):
+    return M * K * 4 + M * K + M * (K // 32) * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch the decode layers one by one")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl):
+    """Time the CPU oracle on a bounded sample of the same workloads."""
+    import numpy as np
+    from oracle import oracle as orc
+    threads = orc.get_threads()
+    out = {"kind": "oracle", "cores": threads}
+    # GEMV: the oracle's fp64 GEMV on a sample of the decode projection set (one
+    # layer's q, k, v, o, gate, up, down at M = 1), packing excluded from timing
+    cases = []
+    for idx, (name, K, N) in enumerate(wl.DECODE_PROJECTIONS[:7]):
+        W, x = wl.gemv_case(idx, 1, N, K)
+        qs, sm = orc.q4_pack(W.numpy())
+        cases.append((x.numpy(), qs, sm, K, gemv_bytes(1, N, K)))
+    nbytes, secs, passes = 0, 0.0, 0
+    while passes < 3 or secs < 8.0:   # whole passes over the layer, >= 8 s of work
+        for (xn, qs, sm, K, b) in cases:
+            t0 = time.perf_counter()
+            orc.q4_gemv(xn, qs, sm, K)
+            secs += time.perf_counter() - t0
+            nbytes += b
+        passes += 1
+    gemv_gbs = nbytes / secs / 1e9
+    # MMQ: the oracle's fp64 MMQ on 256 of the 2048 activation rows of the
+    # 4096 -> 12288 layer (ops counted for those rows only)
+    c = wl.MMQ_2048[0]
+    rows = 256
+    W, x = wl.mmq_case(c["seed"], rows, c["N"], c["K"], True)
+    qs, sm = orc.q4_pack(W.numpy())
+    qa, ds = orc.q8_1_quantize(x.numpy())
+    t0 = time.perf_counter()
+    orc.q4_mmq(qa, ds, qs, sm, c["K"])
+    ms = time.perf_counter() - t0
+    out.update({
+        "value": round(gemv_gbs, 3), "unit": "GB/s",
+        "sample": "oracle q4_gemv (fp64) over %d passes of one layer of the decode projection "
+                  "set (q,k,v,o,gate,up,down, M=1, %.1f MB per pass) in %.2f s; oracle q4_mmq on "
+                  "%d of 2048 rows of the 4096->12288 prefill layer in %.2f s"
+                  % (passes, nbytes / passes / 1e6, secs, rows, ms),
+        "mmq_tops": round(2.0 * rows * c["N"] * c["K"] / ms / 1e12, 6),
+    })
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the multi-GPU sharding is a design note, not an implementation)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_matmul_q4_amd as q4
+    from bit_quantized_matmul_q4_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------ setup ----
+    def packed(seed, N, K):
+        g = wl.generator(seed, dev)
+        W = wl.draw_weights(g, N, K, dev)
+        qs, sm = q4.q4_pack(W)
+        del W
+        return qs, sm
+
+    gx = wl.generator(12345, dev)
+    xs = {K: wl.draw_activations(gx, 1, K, False, dev) for K in (2560, 4096, 9216)}
+    layers = []
+    for layer in range(LAYERS):
+        projs = []
+        for k, (name, K, N) in enumerate(wl.DECODE_PROJECTIONS[:7]):
+            qs, sm = packed(8 * layer + k, N, K)
+            y = torch.empty((1, N), dtype=torch.float32, device=dev)
+            projs.append((name, K, N, qs, sm, y))
+        layers.append(projs)
+    _, Kl, Nl = wl.DECODE_PROJECTIONS[7]
+    lm_qs, lm_sm = packed(7, Nl, Kl)
+    lm_y = torch.empty((1, Nl), dtype=torch.float32, device=dev)
+    layer_bytes = sum(gemv_bytes(1, N, K) for (_, K, N) in wl.DECODE_PROJECTIONS[:7])
+    lm_bytes = gemv_bytes(1, Nl, Kl)
+    decode_bytes = LAYERS * layer_bytes + lm_bytes
+
+    pre = []
+    for c in wl.MMQ_2048 + [dict(wl.MMQ_512, name="m512")]:
+        W, x = wl.mmq_case(c["seed"], c["M"], c["N"], c["K"], c["outliers"], dev)
+        qs, sm = q4.q4_pack(W)
+        del W
+        qa = torch.empty((c["M"], c["K"]), dtype=torch.int8, device=dev)
+        ds = torch.empty((c["M"], c["K"] // 32, 2), dtype=torch.float16, device=dev)
+        y = torch.empty((c["M"], c["N"]), dtype=torch.float32, device=dev)
+        ws_n = q4.q4_mmq_workspace_bytes(c["M"], c["N"], c["K"])
+        ws = torch.empty((max(ws_n, 1),), dtype=torch.uint8, device=dev)
+        pre.append((c, x, qa, ds, qs, sm, y, ws))
+    # a plain device copy of known size: reference for the HBM byte counters
+    cp_src = torch.empty((64 << 20,), dtype=torch.float32, device=dev).fill_(1.0)
+    cp_dst = torch.empty_like(cp_src)
+    torch.cuda.synchronize()
+
+    def decode_layers():
+        for projs in layers:
+            for (name, K, N, qs, sm, y) in projs:
+                q4.q4_gemv(xs[K], qs, sm, y=y)
+
+    def lm_head():
+        q4.q4_gemv(xs[Kl], lm_qs, lm_sm, y=lm_y)
+
+    decode_layers()  # warm the per-device property cache before any capture
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode_layers()
+        torch.cuda.synchronize()
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    n_ev = 3 + 4 * len(pre)
+
+    def step(ev):
+        ev[0].record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            decode_layers()
+        ev[1].record(stream)
+        lm_head()
+        ev[2].record(stream)
+        i = 3
+        for (c, x, qa, ds, qs, sm, y, ws) in pre:
+            ev[i].record(stream)
+            q4.q8_1_quantize(x, qa, ds)
+            ev[i + 1].record(stream)
+            q4.q4_mmq_gemm(qa, ds, qs, sm, y=y, workspace=ws)
+            ev[i + 2].record(stream)
+            i += 4  # (the 4th slot keeps the layout uniform)
+        return ev
+
+    for _ in range(args.warmup):
+        step([E() for _ in range(n_ev)])
+    cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------ timed ----
+    events = [[E() for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def med(vals):
+        v = sorted(vals)
+        return v[len(v) // 2]
+
+    layers_ms = med([e[0].elapsed_time(e[1]) for e in events])
+    lm_ms = med([e[1].elapsed_time(e[2]) for e in events])
+    decode_ms = med([e[0].elapsed_time(e[2]) for e in events])
+    mmq_rep = {}
+    for k, (c, *_rest) in enumerate(pre):
+        i = 3 + 4 * k
+        q_ms = med([e[i].elapsed_time(e[i + 1]) for e in events])
+        g_ms = med([e[i + 1].elapsed_time(e[i + 2]) for e in events])
+        ops = 2.0 * c["M"] * c["N"] * c["K"]
+        mmq_rep["M%d_%s" % (c["M"], c["name"])] = {
+            "M": c["M"], "K": c["K"], "N": c["N"],
+            "mmq_us": round(g_ms * 1e3, 2), "tops": round(ops / (g_ms * 1e-3) / 1e12, 2),
+            "frac_i8_peak": round(ops / (g_ms * 1e-3) / 1e12 / I8_PEAK_TOPS, 4),
+            "q8_1_us": round(q_ms * 1e3, 2),
+            "q8_1_gbs": round(q8_bytes(c["M"], c["K"]) / (q_ms * 1e-3) / 1e9, 1),
+            "tops_incl_q8_1": round(ops / ((g_ms + q_ms) * 1e-3) / 1e12, 2),
+        }
+    step_ms = wall / args.steps * 1e3
+    value = decode_bytes / (decode_ms * 1e-3) / 1e9
+    lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
+    big = mmq_rep["M2048_gate_up"]
+
+    out = {
+        "metric": "Q4 GEMV effective HBM GB/s (M=1) + MMQ prefill TOPS (M=512/2048)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4 x f16(hi+lo) -> f32 (GEMV); i8 x u4 -> i32 (MMQ)",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; random weights of the stated shapes)",
+        "config": {
+            "workload": "decode token of a ~4B dense transformer at M=1: 36 layers x "
+                        "{q,k,v 2560->4096/1024/1024, o 4096->2560, gate,up 2560->9216, down 9216->2560} "
+                        "+ lm_head 2560->151936, 4-bit group-256; plus MMQ prefill M=2048 "
+                        "(4096->12288, 12288->4096) and M=512 (2560->9216)",
+            "decode_bytes_per_step": decode_bytes,
+            "graph": graph is not None,
+        },
+        "decode": {
+            "layers_us": round(layers_ms * 1e3, 1),
+            "layers_gbs": round(LAYERS * layer_bytes / (layers_ms * 1e-3) / 1e9, 1),
+            "lm_head_us": round(lm_ms * 1e3, 2),
+            "lm_head_gbs": round(lm_gbs, 1),
+            "tokens_per_s_weights_only": round(1e3 / decode_ms, 1),
+        },
+        "roofline": {
+            "kernel": "k_gemv_dot2 (lm_head launch, M=1, K=2560, N=151936)",
+            "bound": "hbm",
+            "achieved": round(lm_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "mmq_prefill": dict(mmq_rep, roofline={
+            "kernel": "k_mmq (M=2048, K=4096, N=12288)", "bound": "mfma",
+            "achieved": big["tops"], "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+            "frac": round(big["tops"] / I8_PEAK_TOPS, 4)}),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,86 @@
+// q4mi_device.h -- device-side helpers shared by the library's kernels
+// (gfx950 / CDNA4, wave64).  Internal to libq4mi; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4mi {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 256;  // weights per (scale, minimum) group along K
+constexpr int kBlock = 32;   // activations per Q8_1 block along K
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef int int16_t_v __attribute__((ext_vector_type(16)));
+
+// DPP controls (GCN/CDNA encoding of the dpp_ctrl field).
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int ctrl>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 ctrl, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G = 8 or 16) of one DPP row; every lane
+// of the group ends with the same bits (each step adds a commuted pair).
+template <int G>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(G == 8 || G == 16, "group of 8 or 16 lanes");
+    v += dpp_f32<kDppQuadSwap1>(v);
+    v += dpp_f32<kDppQuadSwap2>(v);
+    v += dpp_f32<kDppRowHalfMirror>(v);
+    if (G == 16) v += dpp_f32<kDppRowMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
+{
+    // v_cvt_f16_f32: IEEE round-to-nearest-even, fp16 subnormals kept.
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
+// Raw buffer loads.  The descriptor carries the buffer size; a load whose
+// bytes fall outside it returns zeros, so edge rows need no branch (a branch
+// around a load makes the compiler wait for every outstanding load).
+// 0x00020000 is the gfx9-family descriptor word 3 (32-bit data format).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off)
+{
+    const int4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return __builtin_bit_cast(uint4, v);
+}
+
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+// Largest byte count a single launch addresses through one descriptor with
+// 32-bit offsets; launchers split bigger weight matrices into row ranges.
+constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
+
+}  // namespace q4mi

@@ -1,0 +1,32 @@
+// q4mi_kernels.h -- launchers of the library's kernels (internal to libq4mi).
+// Arguments are validated by the C-ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4mi {
+
+struct DeviceInfo {
+    int num_cus;
+    int lds_bytes;
+};
+
+hipError_t launch_q4_pack(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm,
+                          int num_cus, hipStream_t stream);
+hipError_t launch_q8_1_quantize(const float *x, int64_t M, int64_t K, int8_t *qa, uint16_t *ds,
+                                int num_cus, hipStream_t stream);
+
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                       int K, float *y, void *workspace, const DeviceInfo &dev, hipStream_t stream);
+
+size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                      const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
+                      const DeviceInfo &dev, hipStream_t stream);
+hipError_t launch_block_dots(const int8_t *qa, int64_t M, const uint8_t *qs, int64_t N, int K,
+                             int32_t *idot, const DeviceInfo &dev, hipStream_t stream);
+
+}  // namespace q4mi

@@ -1,0 +1,129 @@
+// quantize.hip -- weight packing (4-bit, group 256, fp16 scale + minimum) and
+// Q8_1 activation quantization for gfx950.
+//
+// Both kernels are HBM-streaming passes that must reproduce the defining fp32
+// arithmetic bit for bit: every decision (min/max, the fp32 divisions, the
+// fp16 rounding, the round-half-to-even of the codes) uses correctly rounded
+// IEEE operations (__fdiv_rn, __fsub_rn, __fmul_rn, rintf, v_cvt_f16_f32 with
+// round-to-nearest-even) and nothing is contracted into an FMA.
+//
+// Formats: the HFQ4-G256 weight format and the Q8_1 activation format of the
+// hipfire MMQ-prefill note (ai-navigate-news.com article, list of changes);
+// the byte layout is this library's (see q4mi.h).
+#include "q4mi_device.h"
+#include "q4mi_kernels.h"
+
+namespace q4mi {
+
+// One wave per group of 256 weights: lane l holds elements 4l .. 4l+3 (one
+// 16-byte load per lane, 1 KiB per wave).  Codes of elements 32j+i and
+// 32j+i+16 share byte 16j+i, so the lane holding elements 32j+16+4u.. (lane%8
+// >= 4) hands its codes to lane-4, which writes one dword of four bytes.
+__global__ __launch_bounds__(256) void k_q4_pack(const float *__restrict__ W,
+                                                 uint8_t *__restrict__ qs,
+                                                 uint32_t *__restrict__ sm, int64_t ngroups)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t stride = (int64_t)gridDim.x * (blockDim.x / kWave);
+    for (int64_t grp = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+         grp < ngroups; grp += stride) {
+        // rows are K = 256 * G floats long, so group grp starts at grp * 256
+        const float4 v = *reinterpret_cast<const float4 *>(W + grp * kGroup + lane * 4);
+        float mn = fminf(fminf(v.x, v.y), fminf(v.z, v.w));
+        float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            mn = fminf(mn, __shfl_xor(mn, o));
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+        }
+        mn = __fadd_rn(mn, 0.0f);  // a zero minimum or maximum counts as +0
+        mx = __fadd_rn(mx, 0.0f);
+        const float range = __fsub_rn(mx, mn);
+        const uint16_t s16 = f32_to_f16_bits(__fdiv_rn(range, 15.0f));
+        const uint16_t m16 = f32_to_f16_bits(mn);
+        const float sf = f16_bits_to_f32(s16), mf = f16_bits_to_f32(m16);
+        const float e[4] = {v.x, v.y, v.z, v.w};
+        uint32_t codes = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            int q = 0;
+            if (sf != 0.0f) {
+                const float r = rintf(__fdiv_rn(__fsub_rn(e[t], mf), sf));
+                q = r < 0.0f ? 0 : (r > 15.0f ? 15 : (int)r);
+            }
+            codes |= (uint32_t)q << (8 * t);
+        }
+        const uint32_t high = __shfl_down(codes, 4);
+        if ((lane & 7) < 4) {
+            const int64_t byte = grp * (kGroup / 2) + 16 * (lane >> 3) + 4 * (lane & 7);
+            *reinterpret_cast<uint32_t *>(qs + byte) = codes | (high << 4);
+        }
+        if (lane == 0) sm[grp] = (uint32_t)s16 | ((uint32_t)m16 << 16);
+    }
+}
+
+// Eight lanes per block of 32 activations, four per lane (16-byte loads).
+// The flat element index works across rows because K is a multiple of 32.
+__global__ __launch_bounds__(256) void k_q8_1_quantize(const float *__restrict__ x,
+                                                       int8_t *__restrict__ qa,
+                                                       uint32_t *__restrict__ ds, int64_t nvec4)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec4; i += stride) {
+        // the 8 lanes of one block are all inside or all outside [0, nvec4)
+        const float4 v = reinterpret_cast<const float4 *>(x)[i];
+        float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        const uint16_t d16 = f32_to_f16_bits(__fdiv_rn(amax, 127.0f));
+        const float df = f16_bits_to_f32(d16);
+        const float e[4] = {v.x, v.y, v.z, v.w};
+        uint32_t packed = 0;
+        int sum = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            int a = 0;
+            if (df != 0.0f) {
+                const float r = rintf(__fdiv_rn(e[t], df));
+                a = r < -127.0f ? -127 : (r > 127.0f ? 127 : (int)r);
+            }
+            sum += a;
+            packed |= ((uint32_t)a & 0xFFu) << (8 * t);
+        }
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        reinterpret_cast<uint32_t *>(qa)[i] = packed;
+        if ((i & 7) == 0) {
+            const uint16_t s16 = f32_to_f16_bits(__fmul_rn(df, (float)sum));  // exact product
+            ds[i >> 3] = (uint32_t)d16 | ((uint32_t)s16 << 16);
+        }
+    }
+}
+
+hipError_t launch_q4_pack(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm,
+                          int num_cus, hipStream_t stream)
+{
+    const int64_t ngroups = N * (K / kGroup);
+    int64_t blocks = (ngroups + 3) / 4;
+    const int64_t cap = (int64_t)num_cus * 32;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(k_q4_pack, dim3((unsigned)blocks), dim3(256), 0, stream, W, qs,
+                       reinterpret_cast<uint32_t *>(sm), ngroups);
+    return hipGetLastError();
+}
+
+hipError_t launch_q8_1_quantize(const float *x, int64_t M, int64_t K, int8_t *qa, uint16_t *ds,
+                                int num_cus, hipStream_t stream)
+{
+    const int64_t nvec4 = M * K / 4;
+    int64_t blocks = (nvec4 + 255) / 256;
+    const int64_t cap = (int64_t)num_cus * 16;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(k_q8_1_quantize, dim3((unsigned)blocks), dim3(256), 0, stream, x, qa,
+                       reinterpret_cast<uint32_t *>(ds), nvec4);
+    return hipGetLastError();
+}
+
+}  // namespace q4mi

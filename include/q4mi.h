@@ -1,0 +1,190 @@
+/*
+ * q4mi.h -- C ABI of the MI355X (gfx950) 4-bit weight-quantized matmul library
+ * (libq4mi.so): weight packing, Q8_1 activation quantization, the
+ * dequant-fused GEMV used in decode and the integer "MMQ" GEMM used in prefill.
+ *
+ * Sources of the operations (pages cited by title and section):
+ *   - 4-bit weights in groups of 256 along K with an fp16 scale and an fp16
+ *     minimum per group, two codes per byte: the HFQ4-G256 format named in the
+ *     hipfire MMQ-prefill note (ai-navigate-news.com article, list of changes
+ *     and benchmark table).  The page gives no byte layout; the layout below is
+ *     this library's.
+ *   - Q8_1 pre-quantized activations and i8 matrix-core tile products over
+ *     128x128 output tiles with LDS staging: same note, list of changes.
+ *   - A quantized GEMV arm with fp32 output for few activation rows, and a
+ *     split-K arm for shapes with too few output rows to fill the GPU:
+ *     vllm.cpp issue 5 ("GFX1100-TG200 campaign"), "Starting position".
+ *   - Integer dot products bit-exact against a CPU implementation: vllm.cpp
+ *     pull request 4 ("spec(GFX1100-TG150)"), "Design", correctness policy.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers on the current HIP device, owned
+ *     by the caller.  The library never allocates, frees or synchronizes; work
+ *     is enqueued on `stream` (a hipStream_t passed as void*, NULL = the null
+ *     stream) and the call returns before it runs.
+ *   - Arrays are dense and row-major.  K must be a positive multiple of 256.
+ *   - Arguments are validated before any HIP call; an invalid call enqueues
+ *     nothing and returns a negative Q4_ERR_* code.  A call with M == 0 or
+ *     N == 0 (an empty product) is valid and enqueues nothing.
+ *   - The device must be gfx950 (MI355X class); any other returns Q4_ERR_ARCH.
+ *   - Non-finite inputs are outside the contract.
+ *   - Calls are stateless apart from a per-device cache of device properties,
+ *     and are safe to issue from several host threads.
+ *
+ * Data layouts:
+ *   W   fp32 [N][K]               weights before packing
+ *   qs  u8   [N][K/2]             4-bit codes.  Group g of row n occupies bytes
+ *                                 128g .. 128g+127 of the row.  Within a group,
+ *                                 elements 32j .. 32j+31 take bytes 16j .. 16j+15;
+ *                                 byte i of them holds element 32j+i in its low
+ *                                 nibble and element 32j+i+16 in its high nibble.
+ *   sm  fp16 [N][K/256][2]        (scale, minimum) per group, as IEEE binary16 bits.
+ *                                 Dequantized weight: w = scale * q + minimum.
+ *   x   fp32 [M][K]               activations
+ *   qa  i8   [M][K]               Q8_1 codes
+ *   ds  fp16 [M][K/32][2]         (d, s) per block of 32: x ~= d * a, s = d * sum(a)
+ *   y   fp32 [M][N]               y = x * W^T
+ */
+#ifndef Q4MI_H
+#define Q4MI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4MI_ABI_VERSION 1
+
+enum {
+    Q4_OK = 0,
+    Q4_ERR_ARG = -1,       /* null pointer, bad dimension or size out of range   */
+    Q4_ERR_ALIGN = -2,     /* pointer not aligned as required                     */
+    Q4_ERR_WORKSPACE = -3, /* workspace missing or smaller than required          */
+    Q4_ERR_ARCH = -4,      /* current device is not gfx950                        */
+    Q4_ERR_LAUNCH = -5,    /* the HIP runtime rejected the kernel launch          */
+    Q4_ERR_DEVICE = -6     /* no usable HIP device / runtime query failed         */
+};
+
+/* Largest supported dimensions. */
+#define Q4_MAX_K (1 << 20)          /* K <= 1048576                               */
+#define Q4_MAX_N ((1LL << 31) - 1)  /* N rows of weights                          */
+#define Q4_MAX_M_MMQ ((1LL << 31) - 1)
+#define Q4_GEMV_MAX_M 16            /* q4_gemv takes 1..16 activation rows        */
+
+/* ABI version of the loaded library (Q4MI_ABI_VERSION it was built with). */
+int q4_abi_version(void);
+
+/* Static text for an error code (never NULL). */
+const char *q4_strerror(int code);
+
+/*
+ * q4_pack -- quantize W [N][K] fp32 to 4-bit codes with a scale and a minimum
+ * per group of 256 consecutive k (the HFQ4-G256 weight format of the hipfire
+ * MMQ-prefill note).  For each group, in IEEE fp32 with round-to-nearest-even:
+ *     mn = min w, mx = max w              (a zero counts as +0)
+ *     scale16 = fp16(fp32(mx - mn) / 15), min16 = fp16(mn)
+ *     q = 0 if scale16 == 0, else clamp(rint((w - min16) / scale16), 0, 15)
+ * Output is bit-exact with the definition.
+ *   W:  device fp32 [N][K], 16-byte aligned.
+ *   qs: device u8 [N][K/2], 16-byte aligned.   sm: device u16 [N][K/256][2],
+ *   4-byte aligned.  Outputs must not overlap W.
+ * Errors: Q4_ERR_ARG (null, N < 0, K not a positive multiple of 256, K or N too
+ * large), Q4_ERR_ALIGN, Q4_ERR_ARCH, Q4_ERR_DEVICE, Q4_ERR_LAUNCH.
+ */
+int q4_pack(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm, void *stream);
+
+/*
+ * q8_1_quantize -- quantize activations x [M][K] fp32 to Q8_1 (the activation
+ * format the hipfire MMQ-prefill note pre-quantizes prefill inputs into).
+ * Per block of 32 consecutive k, in IEEE fp32 with round-to-nearest-even:
+ *     amax = max |x|, d16 = fp16(amax / 127)
+ *     a = 0 if d16 == 0, else clamp(rint(x / d16), -127, 127)
+ *     s16 = fp16(d16 * sum(a))
+ * Output is bit-exact with the definition.  K must be a positive multiple of
+ * 32 here (256 for the matmuls that consume it).
+ *   x:  device fp32 [M][K], 16-byte aligned.
+ *   qa: device i8 [M][K], 16-byte aligned.  ds: device u16 [M][K/32][2],
+ *   4-byte aligned.
+ * Errors: Q4_ERR_ARG, Q4_ERR_ALIGN, Q4_ERR_ARCH, Q4_ERR_DEVICE, Q4_ERR_LAUNCH.
+ */
+int q8_1_quantize(const float *x, int64_t M, int64_t K, int8_t *qa, uint16_t *ds, void *stream);
+
+/*
+ * q4_gemv_workspace_bytes -- device workspace q4_gemv needs for this shape
+ * (0 when the shape runs without one).  Pure host function, no HIP call.
+ * Returns 0 for shapes q4_gemv would reject.
+ */
+size_t q4_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * q4_gemv -- y [M][N] = x [M][K] * dequant(qs, sm)^T for 1 <= M <= 16 fp32
+ * activation rows: the dequant-fused decode GEMV with fp32 output (the
+ * "tiny-N f32-out GEMV" and "split-K" arms of vllm.cpp issue 5, "Starting
+ * position"), streaming the 4-bit weights once from HBM.
+ * The fp32 sum order is the library's; results match the fp64 definition
+ * sum_k x[m][k] * (scale * q + minimum) to max|dy| / max|y| <= 2e-3 and
+ * sum(dy^2) / sum(y^2) <= 1e-6 on well-scaled inputs (activations are rounded
+ * to fp16 with a power-of-two scale per 32-element chunk inside the kernel).
+ * Reruns with the same inputs are bit-identical.
+ *   x:  device fp32 [M][K], 16-byte aligned.   qs: device u8 [N][K/2],
+ *   16-byte aligned.   sm: device u16 [N][K/256][2], 4-byte aligned.
+ *   y:  device fp32 [M][N], 4-byte aligned; must not overlap the inputs.
+ *   workspace: device buffer of at least q4_gemv_workspace_bytes(M, N, K)
+ *   bytes, 16-byte aligned (may be NULL when that is 0).  Its contents on entry
+ *   are ignored and on exit are unspecified.  Two calls that run concurrently
+ *   must not share a workspace.
+ * Errors: Q4_ERR_ARG (M outside 0..16, N < 0, K not a positive multiple of
+ * 256, null pointer), Q4_ERR_ALIGN, Q4_ERR_WORKSPACE, Q4_ERR_ARCH,
+ * Q4_ERR_DEVICE, Q4_ERR_LAUNCH.
+ */
+int q4_gemv(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+            int64_t K, float *y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * q4_mmq_workspace_bytes -- device workspace q4_mmq_gemm needs for this shape.
+ * Pure host function.  Returns 0 for shapes q4_mmq_gemm would reject.
+ */
+size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * q4_mmq_gemm -- prefill GEMM on Q8_1 activations (the MMQ path of the hipfire
+ * note: pre-quantized Q8_1 activations, LDS-staged tiles, integer matrix-core
+ * products over 128x128 output tiles):
+ *     y[m][n] = sum_k (d[m][k/32] * a[m][k]) * (scale[n][k/256] * q[n][k] + minimum[n][k/256])
+ * Per-block products sum_{k in block} a * q are exact int32 (i8 MFMA); block
+ * and group scales are applied in fp32.  Results match the fp64 definition to
+ * max|dy| / max|y| <= 2e-3 and NMSE <= 1e-6.  The s field of ds is not read.
+ * Reruns are bit-identical.
+ *   qa: device i8 [M][K], 16-byte aligned.  ds: device u16 [M][K/32][2],
+ *   4-byte aligned.  qs/sm as for q4_gemv.  y: device fp32 [M][N], 4-byte
+ *   aligned.  workspace: at least q4_mmq_workspace_bytes(M, N, K) bytes,
+ *   16-byte aligned (NULL allowed when that is 0); same rules as q4_gemv.
+ * Errors: Q4_ERR_ARG, Q4_ERR_ALIGN, Q4_ERR_WORKSPACE, Q4_ERR_ARCH,
+ * Q4_ERR_DEVICE, Q4_ERR_LAUNCH.
+ */
+int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                const uint16_t *sm, int64_t N, int64_t K, float *y, void *workspace,
+                size_t ws_bytes, void *stream);
+
+/*
+ * q4_mmq_block_dots -- the integer core of q4_mmq_gemm on its own, for
+ * checking it bit-exactly (the "keep-quant integer core" the vllm.cpp TG150
+ * campaign keeps bit-exact against the CPU, pull request 4, "Design"):
+ *     idot[m][n][b] = sum_{k = 32b}^{32b+31} a[m][k] * q[n][k]      (exact int32)
+ * It runs the same i8 MFMA tile code as q4_mmq_gemm with an epilogue that
+ * stores the per-block sums instead of scaling them.
+ *   qa: device i8 [M][K], 16-byte aligned.  qs: device u8 [N][K/2], 16-byte
+ *   aligned.  idot: device i32 [M][N][K/32], 4-byte aligned (M*N*K/32 entries
+ *   must not exceed 2^31).
+ * Errors: Q4_ERR_ARG, Q4_ERR_ALIGN, Q4_ERR_ARCH, Q4_ERR_DEVICE, Q4_ERR_LAUNCH.
+ */
+int q4_mmq_block_dots(const int8_t *qa, int64_t M, const uint8_t *qs, int64_t N, int64_t K,
+                      int32_t *idot, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4MI_H */

@@ -76,6 +76,12 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
+    # thread count: the cores this process may run on, at most 16
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    lib.orc_set_threads(max(1, min(16, ncpu)))
     _lib = lib
     return lib
 
