@@ -55,6 +55,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the decode layers one by one")
+    ap.add_argument("--no-tiny-m", action="store_true", help="skip the tiny-M GEMV sweep")
     return ap.parse_args()
 
 
@@ -99,6 +100,43 @@ def cpu_baseline(wl):
         "mmq_tops": round(2.0 * rows * c["N"] * c["K"] / ms / 1e12, 6),
     })
     return out
+
+
+def tiny_m_sweep(q4, wl, dev, stream, reps=6):
+    """GEMV at M = 1..16 on the lm_head shape (K=4096, N=151936), outside the
+    timed step: two weight copies (2 x 321 MB) alternate so the Infinity Cache
+    cannot serve them; median of per-launch HIP-event times."""
+    import torch
+    c = wl.TINY_M
+    K, N = c["K"], c["N"]
+    copies = []
+    for i in range(2):
+        g = wl.generator(c["seed"] + 100 * i, dev)
+        W = wl.draw_weights(g, N, K, dev)
+        copies.append(q4.q4_pack(W))
+        del W
+    res = {}
+    for M in c["Ms"]:
+        x = wl.draw_activations(wl.generator(M, dev), M, K, False, dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws_n = q4.q4_gemv_workspace_bytes(M, N, K)
+        ws = torch.empty((max(ws_n, 1),), dtype=torch.uint8, device=dev)
+        for i in range(2):
+            q4.q4_gemv(x, *copies[i], y=y, workspace=ws)
+        times = []
+        for r in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            q4.q4_gemv(x, *copies[r % 2], y=y, workspace=ws)
+            b.record(stream)
+            times.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+        nbytes = gemv_bytes(M, N, K)
+        res["M%d" % M] = {"us": round(ms * 1e3, 2), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del copies
+    return res
 
 
 def main():
@@ -278,6 +316,8 @@ def main():
             "achieved": big["tops"], "peak": I8_PEAK_TOPS, "unit": "TOP/s",
             "frac": round(big["tops"] / I8_PEAK_TOPS, 4)}),
     }
+    if not args.no_tiny_m:
+        out["gemv_tiny_m"] = tiny_m_sweep(q4, wl, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

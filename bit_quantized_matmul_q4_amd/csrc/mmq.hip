@@ -4,27 +4,36 @@
 // over 128x128 output tiles).
 //
 //   y[m][n] = sum_g ( s[n][g] * sum_{b in g} d[m][b] * I[m][n][b]
-//                     + mn[n][g] * sum_{b in g} d[m][b] * A[m][b] )
+//                     + mn[n][g] * X[m][g] )
 //   I[m][n][b] = sum_{k in block b} a[m][k] * q[n][k]     (exact int32, MFMA)
-//   A[m][b]    = sum_{k in block b} a[m][k]
+//   X[m][g]    = sum_{b in g} d[m][b] * sum_{k in block b} a[m][k]
 //
 // Design for CDNA4:
 //   * One v_mfma_i32_32x32x32_i8 covers exactly one Q8_1 block (K = 32), so its
-//     int32 result is the block dot I, which the epilogue scales by d[m][b].
-//   * Weights are the A operand (output rows = n), activations the B operand
-//     (output columns = m), so each lane owns one activation row m and its
-//     block scale d[m][b] is a scalar per lane.
-//   * The packed format puts elements i and i+16 of a block in one byte, so
-//     the A operand of lane group 0 (k 0..15) is (chunk & 0x0F0F0F0F) and that
-//     of lane group 1 (k 16..31) is ((chunk >> 4) & 0x0F0F0F0F): K-contiguous
-//     int8 runs, matching a straight 16-byte load of qa for the B operand.
-//   * A workgroup computes a 128x128 tile with 4 waves of 64x64 (2x2 MFMA
-//     tiles).  Each K step stages one 256-wide group in LDS: 128 rows of packed
-//     weights (128 B each), 128 rows of int8 activations (256 B each), the
-//     block scales and the group's (scale, minimum).  Row strides are padded
-//     by 16 bytes so 16-byte LDS reads of consecutive rows hit distinct banks.
-//   * The sum of the activation codes of a block, A[m][b], is taken from the B
-//     operand registers with v_dot4 against 0x01010101 (no extra load).
+//     int32 result is the block dot I.  Weights are the A operand (output rows
+//     n), activations the B operand (output columns m): each lane owns one
+//     activation row m, so the block scale d[m][b] is a scalar per lane.
+//   * Epilogue per output and block: acc += d * (float)I, two VALU ops.  One
+//     32x32x32 int8 MFMA takes 32 cycles per SIMD while one VALU op over its
+//     1024 outputs takes 64, so this epilogue, not the matrix core, bounds the
+//     kernel (at most 25 % of the int8 peak).  Integer accumulation of
+//     D[m][b] * I with 12- or 13-bit integer block scales would need half the
+//     ops but loses too much precision on blocks whose scale is far below the
+//     group's largest (outlier activations); fp32 keeps NMSE near 1e-13.
+//   * Per 128x128 tile and 256-wide K step (one weight group) the workgroup
+//     stages in LDS: the weights unpacked to int8 (each 16-byte packed block
+//     becomes the low-nibble run k 0..15 and the high-nibble run k 16..31), the
+//     int8 activations, the block scales d as fp32, the group's per-row
+//     X[m][g], and the (scale, minimum) pairs as fp32.  Rows are padded to
+//     272 bytes so 16-byte reads of consecutive rows hit distinct banks.
+//     Everything per (row, block) is computed once per workgroup, so the MFMA
+//     loop itself does only LDS reads, MFMAs and the two-op epilogue.
+//   * Loads are raw buffer loads: rows past M or N read as zeros without a
+//     branch.  Tiles are mapped so each XCD works on a contiguous run of
+//     tiles (m fastest), which keeps the shared activation and weight tiles in
+//     that XCD's L2.
+//   * 256 threads = 2 x 2 waves of 64x64 outputs (2x2 MFMA tiles); about 75 KB
+//     of LDS, so two workgroups share a CU and hide each other's staging.
 #include "q4mi_device.h"
 #include "q4mi_kernels.h"
 
@@ -34,180 +43,274 @@ namespace {
 
 constexpr int kTile = 128;             // output tile: 128 (n) x 128 (m)
 constexpr int kBlocks = 8;             // Q8_1 blocks per group (per K step)
-constexpr int kRowA = 128 + 16;        // LDS bytes per weight row per step
-constexpr int kRowB = 256 + 16;        // LDS bytes per activation row per step
-constexpr int kLdsA = kTile * kRowA;
-constexpr int kLdsB = kTile * kRowB;
+constexpr int kRow = 256 + 16;         // LDS bytes per row per step (A and B)
+constexpr int kLdsA = kTile * kRow;
+constexpr int kLdsB = kTile * kRow;
 constexpr int kLdsD = kTile * kBlocks * 4;   // d as fp32
-constexpr int kLdsSM = kTile * 4;            // (scale, minimum) fp16 pair
-constexpr int kLdsTotal = kLdsA + kLdsB + kLdsD + kLdsSM;
+constexpr int kLdsX = kTile * 4;             // X[m][g] as fp32
+constexpr int kLdsSM = kTile * 8;            // (scale, minimum) as fp32
+constexpr int kLdsStage = kLdsA + kLdsB + kLdsD + kLdsX + kLdsSM;
+constexpr int kLdsTotal = kLdsStage;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+// Map the linear workgroup id so that the 8 XCDs (which receive workgroups
+// round-robin) each own a contiguous run of tiles.
+__device__ __forceinline__ int xcd_tile(int pid, int ntiles)
+{
+    constexpr int kXcd = 8;
+    const int per = ntiles / kXcd, rem = ntiles % kXcd;
+    const int xcd = pid % kXcd, local = pid / kXcd;
+    // the first rem XCDs own per + 1 tiles, the others per
+    return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// y and idot point at the sub-problem's first output; ldy / ldi are the row
+// strides (elements) of the full outputs.
+//
+// 512 threads = 8 waves: wave (wn, wm) computes weight rows 64wn .. 64wn+63
+// (two 32-row MFMA tiles) and activation rows 32wm .. 32wm+31 (one tile).
+// One LDS stage of ~75 KB and at most 128 VGPRs per lane, so two workgroups
+// share a CU (4 waves per SIMD) and one's staging and barriers overlap the
+// other's MFMA loop.
 template <bool kDots>
-__global__ __launch_bounds__(256) void k_mmq(const int8_t *__restrict__ qa,
-                                             const uint32_t *__restrict__ ds,
-                                             const uint8_t *__restrict__ qs,
-                                             const uint32_t *__restrict__ sm, float *__restrict__ y,
-                                             int32_t *__restrict__ idot, int M, int N, int K,
-                                             int vec_store)
+__global__ __launch_bounds__(512, kDots ? 1 : 4) void k_mmq(const int8_t *__restrict__ qa,
+                                                            const uint32_t *__restrict__ ds,
+                                                            const uint8_t *__restrict__ qs,
+                                                            const uint32_t *__restrict__ sm,
+                                                            float *__restrict__ y,
+                                                            int32_t *__restrict__ idot, int M, int N,
+                                                            int K, int tiles_m, int64_t ldy,
+                                                            int64_t ldi, int vec_store)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTotal];
-    uint8_t *sA = lds;
-    uint8_t *sB = lds + kLdsA;
-    float *sD = reinterpret_cast<float *>(lds + kLdsA + kLdsB);
-    uint32_t *sSM = reinterpret_cast<uint32_t *>(lds + kLdsA + kLdsB + kLdsD);
+    uint8_t *const sA = lds;
+    uint8_t *const sB = lds + kLdsA;
+    float *const sD = reinterpret_cast<float *>(lds + kLdsA + kLdsB);    // [block][row]
+    float *const sX = reinterpret_cast<float *>(lds + kLdsA + kLdsB + kLdsD);
+    float2 *const sSM = reinterpret_cast<float2 *>(lds + kLdsA + kLdsB + kLdsD + kLdsX);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;      // wave's 64x64 quadrant
+    const int wn = wave & 1, wm = wave >> 1;      // 64 weight rows x 32 activation rows
     const int l32 = lane & 31, half = lane >> 5;  // MFMA column / k-half
-    const int n0 = blockIdx.x * kTile, m0 = blockIdx.y * kTile;
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int mt = tile % tiles_m, nt = tile / tiles_m;
+    const int n0 = nt * kTile, m0 = mt * kTile;
     const int G = K / kGroup, B = K / kBlock;
-    const int64_t rowA = K / 2;
+    const uint32_t rowA = K / 2;
 
-    float yacc[2][2][16];
-    float gacc[2][2][16];
-    float xsum[2];
+    const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowA);
+    const rsrc_t r_qa = make_rsrc(qa, (uint32_t)M * (uint32_t)K);
+    const rsrc_t r_ds = make_rsrc(ds, kDots ? 0u : (uint32_t)M * B * 4u);
+    const rsrc_t r_sm = make_rsrc(sm, kDots ? 0u : (uint32_t)N * G * 4u);
+
+    // ---- stage one group (256 of K) in LDS ----
+    // weights: chunks tid and tid+512 (row idx/8, block idx%8), unpacked to int8;
+    // activations: row tid/4, blocks 2(tid%4) and 2(tid%4)+1, with d and sum(a)
+    auto stage_group = [&](int g) {
+        const int arow = tid >> 2, aq = tid & 3;
+        const int m = min(m0 + arow, M);  // rows past M or N read zeros
+        uint4 w[2], a[4];
+        uint32_t dsw[2] = {0, 0}, psm = 0;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int idx = tid + 512 * p;
+            const int n = min(n0 + (idx >> 3), N);
+            w[p] = buf_load16(r_qs, (uint32_t)n * rowA + g * 128 + (idx & 7) * 16);
+        }
+        const uint32_t base = (uint32_t)m * (uint32_t)K + g * 256 + aq * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = buf_load16(r_qa, base + i * 16);
+        if (!kDots) {
+            const uint32_t o = ((uint32_t)m * B + g * kBlocks + aq * 2) * 4u;
+            dsw[0] = buf_load4(r_ds, o);
+            dsw[1] = buf_load4(r_ds, o + 4);
+            if (tid < kTile) psm = buf_load4(r_sm, ((uint32_t)min(n0 + tid, N) * G + g) * 4u);
+        }
+        __syncthreads();  // every wave is done reading the previous group
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int idx = tid + 512 * p, row = idx >> 3, blk = idx & 7;
+            const uint4 lo = make_uint4(w[p].x & 0x0F0F0F0Fu, w[p].y & 0x0F0F0F0Fu,
+                                        w[p].z & 0x0F0F0F0Fu, w[p].w & 0x0F0F0F0Fu);
+            const uint4 hi = make_uint4((w[p].x >> 4) & 0x0F0F0F0Fu, (w[p].y >> 4) & 0x0F0F0F0Fu,
+                                        (w[p].z >> 4) & 0x0F0F0F0Fu, (w[p].w >> 4) & 0x0F0F0F0Fu);
+            *reinterpret_cast<uint4 *>(sA + row * kRow + blk * 32) = lo;
+            *reinterpret_cast<uint4 *>(sA + row * kRow + blk * 32 + 16) = hi;
+        }
+        float xpart = 0.0f;
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+            const uint4 c0 = a[2 * b2], c1 = a[2 * b2 + 1];
+            *reinterpret_cast<uint4 *>(sB + arow * kRow + aq * 64 + b2 * 32) = c0;
+            *reinterpret_cast<uint4 *>(sB + arow * kRow + aq * 64 + b2 * 32 + 16) = c1;
+            if (!kDots) {
+                int sa = 0;
+                sa = __builtin_amdgcn_sdot4((int)c0.x, 0x01010101, sa, false);
+                sa = __builtin_amdgcn_sdot4((int)c0.y, 0x01010101, sa, false);
+                sa = __builtin_amdgcn_sdot4((int)c0.z, 0x01010101, sa, false);
+                sa = __builtin_amdgcn_sdot4((int)c0.w, 0x01010101, sa, false);
+                sa = __builtin_amdgcn_sdot4((int)c1.x, 0x01010101, sa, false);
+                sa = __builtin_amdgcn_sdot4((int)c1.y, 0x01010101, sa, false);
+                sa = __builtin_amdgcn_sdot4((int)c1.z, 0x01010101, sa, false);
+                sa = __builtin_amdgcn_sdot4((int)c1.w, 0x01010101, sa, false);
+                const float d = f16_bits_to_f32(dsw[b2] & 0xFFFFu);
+                sD[(aq * 2 + b2) * kTile + arow] = d;  // block-major: conflict-free reads
+                xpart = fmaf(d, (float)sa, xpart);
+            }
+        }
+        if (!kDots) {
+            // the row's eight blocks sit in four consecutive lanes
+            xpart += __shfl_xor(xpart, 1);
+            xpart += __shfl_xor(xpart, 2);
+            if (aq == 0) sX[arow] = xpart;
+            if (tid < kTile)
+                sSM[tid] = make_float2(f16_bits_to_f32(psm & 0xFFFFu), f16_bits_to_f32(psm >> 16));
+        }
+        __syncthreads();
+    };
+
+    float yacc[2][16];
 #pragma unroll
     for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) yacc[ta][tb][e] = 0.0f;
+        for (int e = 0; e < 16; ++e) yacc[ta][e] = 0.0f;
 
+    const int arow_w = wm * 32 + l32;  // this lane's activation row in the tile
+#pragma unroll 1
     for (int g = 0; g < G; ++g) {
-        __syncthreads();
-        // ---- stage one group of weights, activations and scales in LDS ----
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {  // weights: 128 rows x 8 x 16 B
-            const int idx = tid + 256 * p, row = idx >> 3, seg = idx & 7;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (n0 + row < N)
-                v = *reinterpret_cast<const uint4 *>(qs + (int64_t)(n0 + row) * rowA + g * 128 + seg * 16);
-            *reinterpret_cast<uint4 *>(sA + row * kRowA + seg * 16) = v;
-        }
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {  // activations: 128 rows x 16 x 16 B
-            const int idx = tid + 256 * p, row = idx >> 4, seg = idx & 15;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (m0 + row < M)
-                v = *reinterpret_cast<const uint4 *>(qa + (int64_t)(m0 + row) * K + g * 256 + seg * 16);
-            *reinterpret_cast<uint4 *>(sB + row * kRowB + seg * 16) = v;
-        }
-        if (!kDots) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {  // block scales d: 128 rows x 8 blocks
-                const int idx = tid + 256 * p, row = idx >> 3, b = idx & 7;
-                float d = 0.0f;
-                if (m0 + row < M)
-                    d = f16_bits_to_f32(ds[(int64_t)(m0 + row) * B + g * kBlocks + b] & 0xFFFFu);
-                sD[row * kBlocks + b] = d;
-            }
-            if (tid < kTile)
-                sSM[tid] = (n0 + tid < N) ? sm[(int64_t)(n0 + tid) * G + g] : 0u;
-        }
-        __syncthreads();
+        stage_group(g);
 
-        // ---- 8 blocks of 32: MFMA + per-block epilogue ----
-        if (!kDots) {
+        // ---- 8 blocks x 2 tiles: MFMA + per-block epilogue ----
+        // the MFMA of the next tile is issued before the epilogue of the last
+        float gacc[2][16];
 #pragma unroll
-            for (int ta = 0; ta < 2; ++ta)
+        for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
+            for (int e = 0; e < 16; ++e) gacc[ta][e] = 0.0f;
+        const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        auto a_op = [&](int b, int ta) {
+            return *reinterpret_cast<const v4i *>(sA + (wn * 64 + ta * 32 + l32) * kRow + b * 32 + half * 16);
+        };
+        auto b_op = [&](int b) {
+            return *reinterpret_cast<const v4i *>(sB + arow_w * kRow + b * 32 + half * 16);
+        };
+        auto epilogue = [&](const v16i &I, int ta, float d, int b) {
+            if (kDots) {
+                const int m = m0 + arow_w;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) gacc[ta][tb][e] = 0.0f;
-            xsum[0] = xsum[1] = 0.0f;
-        }
+                for (int e = 0; e < 16; ++e) {
+                    const int n = n0 + wn * 64 + ta * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+                    if (m < M && n < N) idot[(int64_t)m * ldi + (int64_t)n * B + g * kBlocks + b] = I[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) gacc[ta][e] = fmaf(d, (float)I[e], gacc[ta][e]);
+            }
+        };
+        v4i a1 = a_op(0, 1), bv = b_op(0);
+        float dcur = kDots ? 0.0f : sD[arow_w];
+        v16i prev = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op(0, 0), bv, zero, 0, 0, 0);
+        float dprev = dcur;
+#pragma unroll
         for (int b = 0; b < kBlocks; ++b) {
-            v4i av[2], bv[2];
-#pragma unroll
-            for (int ta = 0; ta < 2; ++ta) {
-                const int row = wn * 64 + ta * 32 + l32;
-                const uint4 c = *reinterpret_cast<const uint4 *>(sA + row * kRowA + b * 16);
-                const int sh = half * 4;
-                av[ta] = v4i{(int)((c.x >> sh) & 0x0F0F0F0Fu), (int)((c.y >> sh) & 0x0F0F0F0Fu),
-                             (int)((c.z >> sh) & 0x0F0F0F0Fu), (int)((c.w >> sh) & 0x0F0F0F0Fu)};
+            // tile 1 of block b
+            const v16i t1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bv, zero, 0, 0, 0);
+            epilogue(prev, 0, dprev, b);
+            prev = t1;
+            dprev = dcur;
+            if (b + 1 < kBlocks) {
+                // tile 0 of block b+1; its operands are read after the running
+                // sums exist, so no MFMA is hoisted above an earlier epilogue
+                asm volatile("" : "+v"(gacc[0][0]), "+v"(gacc[0][15]), "+v"(gacc[1][0]),
+                             "+v"(gacc[1][15])::"memory");
+                bv = b_op(b + 1);
+                a1 = a_op(b + 1, 1);
+                dcur = kDots ? 0.0f : sD[(b + 1) * kTile + arow_w];
+                const v16i t0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op(b + 1, 0), bv, zero, 0, 0, 0);
+                epilogue(prev, 1, dprev, b);
+                prev = t0;
+                dprev = dcur;
             }
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                const int row = wm * 64 + tb * 32 + l32;
-                bv[tb] = *reinterpret_cast<const v4i *>(sB + row * kRowB + b * 32 + half * 16);
-            }
-            float dm[2] = {0.0f, 0.0f};
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                if (!kDots) {
-                    dm[tb] = sD[(wm * 64 + tb * 32 + l32) * kBlocks + b];
-                    int s = 0;
-                    s = __builtin_amdgcn_sdot4(bv[tb].x, 0x01010101, s, false);
-                    s = __builtin_amdgcn_sdot4(bv[tb].y, 0x01010101, s, false);
-                    s = __builtin_amdgcn_sdot4(bv[tb].z, 0x01010101, s, false);
-                    s = __builtin_amdgcn_sdot4(bv[tb].w, 0x01010101, s, false);
-                    s += __shfl_xor(s, 32);
-                    xsum[tb] = fmaf(dm[tb], (float)s, xsum[tb]);
-                }
-            }
-#pragma unroll
-            for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-                    const v16i I = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[ta], bv[tb], zero, 0, 0, 0);
-                    if (kDots) {
-                        const int m = m0 + wm * 64 + tb * 32 + l32;
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int n = n0 + wn * 64 + ta * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-                            if (m < M && n < N)
-                                idot[((int64_t)m * N + n) * B + g * kBlocks + b] = I[e];
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            gacc[ta][tb][e] = fmaf(dm[tb], (float)I[e], gacc[ta][tb][e]);
-                    }
-                }
         }
+        epilogue(prev, 1, dprev, kBlocks - 1);
+
         if (!kDots) {
             // ---- group epilogue: weight scale and minimum ----
+            const float xm = sX[arow_w];
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const uint32_t smv = sSM[wn * 64 + ta * 32 + 8 * (e >> 2) + 4 * half + (e & 3)];
-                    const float sf = f16_bits_to_f32(smv & 0xFFFFu), mf = f16_bits_to_f32(smv >> 16);
-#pragma unroll
-                    for (int tb = 0; tb < 2; ++tb)
-                        yacc[ta][tb][e] = fmaf(sf, gacc[ta][tb][e], fmaf(mf, xsum[tb], yacc[ta][tb][e]));
+                    const float2 smv = sSM[wn * 64 + ta * 32 + 8 * (e >> 2) + 4 * half + (e & 3)];
+                    yacc[ta][e] = fmaf(smv.x, gacc[ta][e], fmaf(smv.y, xm, yacc[ta][e]));
                 }
         }
     }
 
     if (!kDots) {
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const int m = m0 + wm * 64 + tb * 32 + l32;
-            if (m >= M) continue;
+        const int m = m0 + arow_w;
+        if (m < M) {
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const int n = n0 + wn * 64 + ta * 32 + 8 * r4 + 4 * half;
-                    float *dst = y + (int64_t)m * N + n;
+                    float *dst = y + (int64_t)m * ldy + n;
                     if (vec_store && n + 3 < N) {
                         *reinterpret_cast<float4 *>(dst) =
-                            make_float4(yacc[ta][tb][4 * r4], yacc[ta][tb][4 * r4 + 1],
-                                        yacc[ta][tb][4 * r4 + 2], yacc[ta][tb][4 * r4 + 3]);
+                            make_float4(yacc[ta][4 * r4], yacc[ta][4 * r4 + 1], yacc[ta][4 * r4 + 2],
+                                        yacc[ta][4 * r4 + 3]);
                     } else {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            if (n + i < N) dst[i] = yacc[ta][tb][4 * r4 + i];
+                            if (n + i < N) dst[i] = yacc[ta][4 * r4 + i];
                     }
                 }
         }
     }
+}
+
+// Run over sub-problems whose weights (N rows) and activations (M rows) each
+// stay below 2 GiB, the reach of a buffer descriptor with 32-bit offsets.
+hipError_t run_tiles(bool dots, const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                     const uint16_t *sm, int64_t N, int K, float *y, int32_t *idot,
+                     hipStream_t stream)
+{
+    const int64_t n_max = ((kMaxBufferBytes - 1) / (K / 2)) / kTile * kTile;
+    const int64_t m_max = ((kMaxBufferBytes - 1) / K) / kTile * kTile;
+    const int B = K / kBlock;
+    for (int64_t m0 = 0; m0 < M; m0 += m_max) {
+        const int64_t mm = M - m0 < m_max ? M - m0 : m_max;
+        for (int64_t n0 = 0; n0 < N; n0 += n_max) {
+            const int64_t nn = N - n0 < n_max ? N - n0 : n_max;
+            const int tiles_m = (int)((mm + kTile - 1) / kTile);
+            const int64_t tiles = (int64_t)tiles_m * ((nn + kTile - 1) / kTile);
+            if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+            const int8_t *qa0 = qa + m0 * K;
+            const uint8_t *qs0 = qs + n0 * (K / 2);
+            if (dots) {
+                hipLaunchKernelGGL(k_mmq<true>, dim3((unsigned)tiles), dim3(512), 0, stream, qa0,
+                                   (const uint32_t *)nullptr, qs0, (const uint32_t *)nullptr,
+                                   (float *)nullptr, idot + (m0 * N + n0) * B, (int)mm, (int)nn, K,
+                                   tiles_m, (int64_t)0, N * B, 0);
+            } else {
+                float *y0 = y + m0 * N + n0;
+                const int vec_store = (N % 4 == 0) && (nn % 4 == 0) &&
+                                      ((reinterpret_cast<uintptr_t>(y0) & 15) == 0);
+                hipLaunchKernelGGL(k_mmq<false>, dim3((unsigned)tiles), dim3(512), 0, stream, qa0,
+                                   reinterpret_cast<const uint32_t *>(ds + m0 * B * 2), qs0,
+                                   reinterpret_cast<const uint32_t *>(sm + n0 * (K / kGroup) * 2), y0,
+                                   (int32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, N, (int64_t)0,
+                                   vec_store);
+            }
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -218,23 +321,13 @@ hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uin
                       const uint16_t *sm, int64_t N, int K, float *y, void *, const DeviceInfo &,
                       hipStream_t stream)
 {
-    const dim3 grid((unsigned)((N + kTile - 1) / kTile), (unsigned)((M + kTile - 1) / kTile));
-    // 16-byte stores of y need N % 4 == 0 and a 16-byte aligned y
-    const int vec_store = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
-    hipLaunchKernelGGL(k_mmq<false>, grid, dim3(256), 0, stream, qa,
-                       reinterpret_cast<const uint32_t *>(ds), qs,
-                       reinterpret_cast<const uint32_t *>(sm), y, (int32_t *)nullptr, (int)M,
-                       (int)N, K, vec_store);
-    return hipGetLastError();
+    return run_tiles(false, qa, ds, M, qs, sm, N, K, y, nullptr, stream);
 }
 
 hipError_t launch_block_dots(const int8_t *qa, int64_t M, const uint8_t *qs, int64_t N, int K,
                              int32_t *idot, const DeviceInfo &, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((N + kTile - 1) / kTile), (unsigned)((M + kTile - 1) / kTile));
-    hipLaunchKernelGGL(k_mmq<true>, grid, dim3(256), 0, stream, qa, (const uint32_t *)nullptr, qs,
-                       (const uint32_t *)nullptr, (float *)nullptr, idot, (int)M, (int)N, K, 0);
-    return hipGetLastError();
+    return run_tiles(true, qa, nullptr, M, qs, nullptr, N, K, nullptr, idot, stream);
 }
 
 }  // namespace q4mi
