@@ -1,48 +1,46 @@
 // gemv.hip -- dequant-fused GEMV for decode: y[m][n] = sum_k x[m][k] * w[n][k]
-// with 4-bit group-256 weights, 1..16 fp32 activation rows, fp32 output.
-//
-// This is the "tiny-N f32-out GEMV" / "split-K GEMM" arm pair of the vllm.cpp
-// decode campaign (vllm.cpp issue 5, "Starting position") re-designed for
-// gfx950.  It is bound by HBM: every weight byte is read once (0.516 B per
-// weight), so the kernels are built around coalesced 16-byte loads and a VALU
-// budget of about 2.5 lane-ops per weight (256 CUs x 64 lanes x 2.4 GHz
-// against 8 TB/s).
+// with 4-bit group-256 weights, 1..16 fp32 activation rows, fp32 output (the
+// "tiny-N f32-out GEMV" and "split-K" arms of the decode work on the llama.cpp
+// / hipfire pages, "Starting position"), designed for gfx950.  It is bound by
+// HBM: every weight byte is read once (0.516 B per weight), so the kernels are
+// built around coalesced 16-byte buffer loads kept in flight in register rings.
 //
 // Shared techniques:
 //   * Nibble widening by masking alone.  A dword of qs holds 8 codes; masking
 //     it with 0x000F000F or 0x00F000F0 leaves two codes in the mantissas of two
 //     fp16 halves, i.e. the exact fp16 subnormals q * 2^-24 and q * 2^-20
-//     (widening codes to fp16 subnormals follows the gfx942 trick of the vLLM
-//     Octave KV page, "Design choices", where one v_perm makes each code byte
-//     an exact fp16 subnormal).  Activations paired with the high nibbles are
-//     stored pre-multiplied by 2^-4 so both land on one scale.
-//   * Activations are split into an fp16 "hi" part and an fp16 "lo" residual
-//     (about 22 significant bits) after scaling each chunk (arm A) or group
-//     (arm B) by a power of two that puts its largest magnitude in
-//     [2^14, 2^15).  A single fp16 copy is not accurate enough: scale * q has
-//     a large mean that cancels against minimum * sum(x), which amplifies the
-//     fp16 rounding of x about threefold in the result.
-//   * Per group: y += (scale * 2^(24+e)) * dot + minimum * sum(x_group), the
-//     minimum term using the exact fp32 sum of the activations.
+//     (the same idea as the gfx942 KV-cache page, "Design choices", where one
+//     v_perm makes each code byte an exact fp16 subnormal).  Activations paired
+//     with the high nibbles are stored pre-multiplied by 2^-4, so both land on
+//     one scale.
+//   * Activations become fp16 after scaling a chunk (arm A: 32 elements) or a
+//     group (arm B: 256) by a power of two that puts its largest magnitude in
+//     [2^14, 2^15).  fp16 rounding alone is not accurate enough: scale * q has
+//     mean about 7.5 * scale, which cancels against minimum * sum(x) and
+//     amplifies the rounding of x.  So each chunk / group also carries
+//     c = 7.5 * sum(x - fp16(x)), computed exactly in fp32; it restores the
+//     rounding's share on the mean code, and what remains is
+//     sum (x - fp16(x)) * (q - 7.5) over centred codes (NMSE ~5e-8 on the
+//     N(0, 0.02) / N(0, 1) workloads, against a 1e-6 budget).
+//   * Per group: y += scale * (f * dot + c) + minimum * X, where f = 2^(24+e)
+//     undoes the scalings and X is the exact fp32 sum of the activations.
 //   * Fixed reduction orders, no atomics: reruns are bit-identical.
 //
-// Arm A, "dot2" (M = 1, VALU): G lanes (16, or 8 when K/32 is not a multiple of
-// 16) share one row; lane j owns the 16-byte chunks s*G*CPT + t*G + j (t < CPT)
-// of every row, a fixed K-slice s, so its activations (hi and lo, 2*CPT*16
-// VGPRs) are loaded once and reused for every row.  v_dot2_f32_f16 multiplies
-// a widened pair by the activation pair: 0.63 unpack + 1 multiply op per
-// weight.  Row partials are reduced across the G lanes with DPP and, with
-// several K-slices, across waves through LDS in slice order.
+// Arm A, "dot2" (M = 1, VALU): the workgroup converts x once into LDS; G lanes
+// (16, or 8 when K/32 is not a multiple of 16) share a weight row, lane j owning
+// its 16-byte chunks j, j+G, ...; v_dot2_f32_f16 multiplies a widened pair by an
+// activation pair (0.63 unpack + 0.5 multiply op per weight).  Row partials are
+// summed across the G lanes with DPP.  Waves are persistent, with the same
+// number of row batches each.
 //
-// Arm B, "mfma" (M = 2..16, matrix cores): with several activation rows the
-// VALU can no longer keep up with HBM, so the contraction goes to
-// v_mfma_f32_16x16x32_f16: A = 16 weight rows x 32 k (one qs dword per lane,
-// widened as above), B = 32 k x 16 activation columns (hi, then lo, chained
-// into one fp32 accumulator).  Each wave keeps the B operands of GPW groups of
-// K in registers and visits every 16-row block of the workgroup's tile; the
-// waves' per-group partials meet in LDS once per row block.  When K has more
-// groups than one workgroup's waves hold, the K range is split over
-// workgroups and a second pass sums the fp32 partials in split order.
+// Arm B, "mfma" (M = 2..16, matrix cores): v_mfma_f32_16x16x32_f16 with the
+// activations as A (16 rows, zeros past M) read from an LDS image the
+// workgroup builds once, and 16 weight rows as B straight from the widened
+// registers.  Each wave streams (16-row unit, group) items through a ring of
+// register slots refilled as soon as they are consumed, so the weights of
+// several items stay in flight with no barrier in the loop.  K is split over
+// workgroups when LDS cannot hold all of it or N gives too few units; a second
+// pass then sums the fp32 partials in split order.
 #include "q4mi_device.h"
 #include "q4mi_kernels.h"
 
@@ -66,12 +64,6 @@ __device__ __forceinline__ void widen(uint32_t w, uint32_t (&p)[4])
     p[3] = w8 & 0x00F000F0u;
 }
 
-// element index (within a chunk) of slot (pair p, half h) of dword t
-__device__ __forceinline__ int slot_elem(int t, int p, int h)
-{
-    return ((p & 1) ? 16 : 0) + 4 * t + ((p & 2) ? 1 : 0) + 2 * h;
-}
-
 // power-of-two exponent sc with amax * 2^-sc in [2^14, 2^15)
 __device__ __forceinline__ int chunk_exp(float amax)
 {
@@ -80,19 +72,16 @@ __device__ __forceinline__ int chunk_exp(float amax)
     return e - 15;
 }
 
-__device__ __forceinline__ void split_hi_lo(float v, _Float16 &hi, _Float16 &lo)
-{
-    hi = (_Float16)v;
-    lo = (_Float16)(v - (float)hi);  // exact residual, rounded to fp16
-}
-
 // ------------------------------------------------------------------ arm A --
 
-// LDS image of the activations for arm A: per 32-element chunk, 16 hi dwords
-// and 16 lo dwords (fp16 pairs in widening order), the chunk's 2^(24+e) factor
-// and its fp32 sum.  The 144-byte stride (128 + 16) makes 16-byte reads of
-// consecutive chunks by consecutive lanes fall on distinct LDS banks.
-constexpr int kChunkLds = 144;
+// LDS image of the activations for arm A: per 32-element chunk, 16 dwords of
+// fp16 pairs in widening order and a float4 (f, X, c, 0): f = 2^(24+e) undoes
+// the chunk's power-of-two scaling and the subnormal weights, X is the fp32
+// sum of the chunk and c = 7.5 * sum of (x - hi), the centred codes' share of
+// the fp16 rounding of x (the error left is sum (x - hi)(q - 7.5)).  The
+// 80-byte stride puts 16-byte reads of consecutive chunks by consecutive lanes
+// on distinct LDS banks.
+constexpr int kChunkLds = 80;
 
 // Four threads per chunk; thread i converts dword i of it (elements 4i..4i+3
 // and 16+4i..16+4i+3).  C is a multiple of 8 and blockDim a multiple of 64,
@@ -114,19 +103,22 @@ __device__ __forceinline__ void fill_x_chunks(const float *__restrict__ x, int C
         const float ls = ldexpf(1.0f, -sc), hs = ldexpf(1.0f, -sc - 4);
         // pairs of dword i: (4i, 4i+2) (16+4i, 16+4i+2) (4i+1, 4i+3) (16+4i+1, 16+4i+3)
         const float v[8] = {a.x * ls, a.z * ls, b.x * hs, b.z * hs, a.y * ls, a.w * ls, b.y * hs, b.w * hs};
-        uint32_t hw[4], lw[4];
+        uint32_t hw[4];
+        float dl = 0.0f, dh = 0.0f;  // residuals of low / high slots, in scaled units
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            _Float16 h0, l0, h1, l1;
-            split_hi_lo(v[2 * p], h0, l0);
-            split_hi_lo(v[2 * p + 1], h1, l1);
+            const _Float16 h0 = (_Float16)v[2 * p], h1 = (_Float16)v[2 * p + 1];
+            const float r = (v[2 * p] - (float)h0) + (v[2 * p + 1] - (float)h1);
+            if (p & 1) dh += r; else dl += r;
             hw[p] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
-            lw[p] = __builtin_bit_cast(uint32_t, half2_t{l0, l1});
         }
+        float delta = ldexpf(dl, sc) + ldexpf(dh, sc + 4);
+        delta += __shfl_xor(delta, 1);
+        delta += __shfl_xor(delta, 2);
         uint8_t *dst = lds + c * kChunkLds;
         *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4 *>(dst + 64 + 16 * i) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        if (i == 0) *reinterpret_cast<float2 *>(dst + 128) = make_float2(ldexpf(1.0f, 24 + sc), sum);
+        if (i == 0)
+            *reinterpret_cast<float4 *>(dst + 64) = make_float4(ldexpf(1.0f, 24 + sc), sum, 7.5f * delta, 0.0f);
     }
 }
 
@@ -181,23 +173,18 @@ __global__ __launch_bounds__(256) void k_gemv_dot2(const float *__restrict__ x,
 #pragma unroll
         for (int t = 0; t < CB; ++t) {
             // The partial sums of chunk t-1 must exist before chunk t's
-            // activation reads are issued: only one chunk's 32 activation
+            // activation reads are issued: only one chunk's 16 activation
             // registers are live, and the loads refilled below stay in flight.
 #pragma unroll
             for (int u = 0; u < U; ++u) asm volatile("" : "+v"(p[u])::"memory");
             const int c = j + G * (pass * CB + t);
             const uint8_t *xc = xl + c * kChunkLds;
-            uint4 hv[4], lv[4];
+            uint4 hv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                hv[i] = *reinterpret_cast<const uint4 *>(xc + 16 * i);
-                lv[i] = *reinterpret_cast<const uint4 *>(xc + 64 + 16 * i);
-            }
-            const float2 fx = *reinterpret_cast<const float2 *>(xc + 128);
+            for (int i = 0; i < 4; ++i) hv[i] = *reinterpret_cast<const uint4 *>(xc + 16 * i);
+            const float4 fx = *reinterpret_cast<const float4 *>(xc + 64);
             const uint32_t xh[16] = {hv[0].x, hv[0].y, hv[0].z, hv[0].w, hv[1].x, hv[1].y, hv[1].z, hv[1].w,
                                      hv[2].x, hv[2].y, hv[2].z, hv[2].w, hv[3].x, hv[3].y, hv[3].z, hv[3].w};
-            const uint32_t xo[16] = {lv[0].x, lv[0].y, lv[0].z, lv[0].w, lv[1].x, lv[1].y, lv[1].z, lv[1].w,
-                                     lv[2].x, lv[2].y, lv[2].z, lv[2].w, lv[3].x, lv[3].y, lv[3].z, lv[3].w};
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float acc = 0.0f;
@@ -207,15 +194,12 @@ __global__ __launch_bounds__(256) void k_gemv_dot2(const float *__restrict__ x,
                     uint32_t pw[4];
                     widen(w4[d], pw);
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
+                    for (int k = 0; k < 4; ++k)
                         acc = __builtin_amdgcn_fdot2(as_half2(pw[k]), as_half2(xh[4 * d + k]), acc, false);
-                        acc = __builtin_amdgcn_fdot2(as_half2(pw[k]), as_half2(xo[4 * d + k]), acc, false);
-                    }
                 }
                 const uint32_t sv = smv[u][t];
                 const float sf = f16_bits_to_f32(sv & 0xFFFFu), mf = f16_bits_to_f32(sv >> 16);
-                p[u] = fmaf(sf * fx.x, acc, p[u]);
-                p[u] = fmaf(mf, fx.y, p[u]);
+                p[u] = fmaf(sf, fmaf(fx.x, acc, fx.z), fmaf(mf, fx.y, p[u]));
             }
             // registers of chunk t are consumed: refill them in place with the
             // next item (the fence keeps the loads below the compute, so the
@@ -299,182 +283,211 @@ hipError_t dispatch_dot2(const Dot2Cfg &c, const float *x, const uint8_t *qs, co
 
 // ------------------------------------------------------------------ arm B --
 
-constexpr int kMfmaRows = 16;  // weight rows per MFMA block
+// One workgroup of kBWaves waves per CU holds the activations of its K range in
+// LDS as MFMA A operands (16 activation rows x 32 k per step, fp16, zeros for
+// rows >= M), so every weight byte fetched from HBM meets its activations
+// without another global read.  Weights are the B operand (16 weight rows x 32
+// k), so the lane that loads a weight row also loads that row's scale and
+// minimum and owns the row's outputs.
+constexpr int kBRows = 16;                      // weight rows per unit (one MFMA column block)
+constexpr int kBWaves = 8;                      // waves per workgroup
+constexpr int kBThreads = kBWaves * kWave;
+constexpr int kBMaxGroups = 18;                 // K groups one workgroup holds in LDS
+constexpr int kBGroupLds = 8 * 4 * kBRows * 16; // A image of one group: [step 8][kg 4][m 16] x 16 B
+constexpr int kBFacLds = 3 * kBRows * 4;        // per group: f[16], X[16], c[16] (fp32)
+constexpr int kBDepth = 12;                     // (unit, group) items in flight per wave
+constexpr int kBTargetUnits = 256 * kBWaves;    // units wanted before K is split further
 
-// One 16-row block per step.  Lane l: A row / B column j = l % 16, k-group
-// kg = l / 16 (chunks 2kg, 2kg+1 of each group), D rows 4kg .. 4kg+3.
-template <int GPW>
-__global__ __launch_bounds__(512) void k_gemv_mfma(const float *__restrict__ x,
-                                                   const uint8_t *__restrict__ qs,
-                                                   const uint32_t *__restrict__ sm,
-                                                   float *__restrict__ out, int M, int N, int K,
-                                                   int groups_per_split, int ntiles)
+__host__ __device__ constexpr size_t arm_b_lds_bytes(int gps) { return (size_t)gps * (kBGroupLds + kBFacLds); }
+
+// Activations of groups g0 .. g0+gc-1 into LDS.  32 threads per (row m, group):
+// thread (c, t) converts dword t of chunk c, i.e. elements 32c+4t..32c+4t+3
+// (low nibbles) and 32c+16+4t..+3 (high nibbles, pre-scaled by 2^-4), in the
+// slot order the weight widening produces.  Per (group, row): the factor
+// f = 2^(24+e) that undoes the group's power-of-two scaling and the subnormal
+// weights, X = sum of x, and c = 7.5 * sum of (x - hi): the codes' mean share
+// of the fp16 rounding of x, folded back in exactly (the remaining error is
+// sum (x - hi) (q - 7.5), with centred codes).
+__device__ __forceinline__ void fill_x_groups(const float *__restrict__ x, int M, int K, int g0, int gc,
+                                              uint8_t *lds)
 {
-    extern __shared__ float red[];  // [2][W][16 rows][16 columns]
-    const int W = blockDim.x / kWave;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int j = lane & 15, kg = lane >> 4;
-    const int split = blockIdx.y;
-    const int GK = K / kGroup;
-    const int gbeg = split * groups_per_split;
-    const int gend = min(GK, gbeg + groups_per_split);
-    const int64_t rowbytes = K / 2;
-    float *dst = out + (int64_t)split * M * N;
-
-    half8_t bh[GPW][8], bl[GPW][8];
-    float fsc[GPW], xs[GPW];
-    bool gvalid[GPW];
-
-    // ---- activations of this wave's groups, as B operands (column m = j) ----
-#pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-        const int g = gbeg + wave * GPW + i;
-        gvalid[i] = g < gend;
-        const bool live = gvalid[i] && j < M;
-        float v[64];  // chunks 2kg and 2kg+1 of group g, row j
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (live) f = reinterpret_cast<const float4 *>(x + (int64_t)j * K + g * kGroup + kg * 64)[q];
-            v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    float *fac = reinterpret_cast<float *>(lds + (size_t)gc * kBGroupLds);
+    for (int idx = threadIdx.x; idx < kBRows * gc * 32; idx += blockDim.x) {
+        const int pair = idx >> 5, sub = idx & 31;
+        const int m = pair & (kBRows - 1), gl = pair >> 4;
+        const int c = sub >> 2, t = sub & 3;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (m < M) {
+            const float *xp = x + (int64_t)m * K + (int64_t)(g0 + gl) * kGroup + c * 32;
+            a = *reinterpret_cast<const float4 *>(xp + 4 * t);
+            b = *reinterpret_cast<const float4 *>(xp + 16 + 4 * t);
         }
-        float amax = 0.0f, sum = 0.0f;
+        float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                           fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+        float sum = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
 #pragma unroll
-        for (int q = 0; q < 64; ++q) {
-            amax = fmaxf(amax, fabsf(v[q]));
-            sum += v[q];
+        for (int o = 1; o < 32; o <<= 1) {
+            amax = fmaxf(amax, __shfl_xor(amax, o));
+            sum += __shfl_xor(sum, o);
         }
-        // the four k-groups of column j sit in lanes j, j+16, j+32, j+48
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
         const int sc = chunk_exp(amax);
-        const float lo_s = ldexpf(1.0f, -sc), hi_s = ldexpf(1.0f, -sc - 4);
+        const float ls = ldexpf(1.0f, -sc), hs = ldexpf(1.0f, -sc - 4);
+        // slot order of one widened dword: (4t, 4t+2) (16+4t, 16+4t+2) (4t+1, 4t+3) (16+4t+1, 16+4t+3)
+        const float v[8] = {a.x * ls, a.z * ls, b.x * hs, b.z * hs, a.y * ls, a.w * ls, b.y * hs, b.w * hs};
+        uint32_t hw[4];
+        float dl = 0.0f, dh = 0.0f;  // residuals of low / high slots, in scaled units
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            const int ch = d >> 2, t = d & 3;
-            half8_t h, l;
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const float sc2 = (p & 1) ? hi_s : lo_s;
-                    _Float16 a, b;
-                    split_hi_lo(v[ch * 32 + slot_elem(t, p, hh)] * sc2, a, b);
-                    h[2 * p + hh] = a;
-                    l[2 * p + hh] = b;
-                }
-            bh[i][d] = h;
-            bl[i][d] = l;
+        for (int p = 0; p < 4; ++p) {
+            const _Float16 h0 = (_Float16)v[2 * p], h1 = (_Float16)v[2 * p + 1];
+            const float r = (v[2 * p] - (float)h0) + (v[2 * p + 1] - (float)h1);
+            if (p & 1) dh += r; else dl += r;
+            hw[p] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
         }
-        fsc[i] = ldexpf(1.0f, 24 + sc);
-        xs[i] = sum;
-    }
-
-    int buf = 0;
-    uint4 cur[GPW][2];
-    auto load_block = [&](int tile, uint4 (&dstv)[GPW][2]) {
-        const int n = tile * kMfmaRows + j;
+        float delta = ldexpf(dl, sc) + ldexpf(dh, sc + 4);
 #pragma unroll
-        for (int i = 0; i < GPW; ++i) {
-            const int g = gbeg + wave * GPW + i;
-            if (gvalid[i] && n < N && tile < ntiles) {
-                const uint4 *p = reinterpret_cast<const uint4 *>(qs + (int64_t)n * rowbytes + g * 128 + kg * 32);
-                dstv[i][0] = p[0];
-                dstv[i][1] = p[1];
-            } else {
-                dstv[i][0] = make_uint4(0, 0, 0, 0);
-                dstv[i][1] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    load_block(blockIdx.x, cur);
-
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        uint4 nxt[GPW][2];
-        load_block(tile + gridDim.x, nxt);  // prefetch the next row block
-
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < GPW; ++i) {
-            const int g = gbeg + wave * GPW + i;
-            float4_t acc = {0.f, 0.f, 0.f, 0.f};
-            const uint32_t w8[8] = {cur[i][0].x, cur[i][0].y, cur[i][0].z, cur[i][0].w,
-                                    cur[i][1].x, cur[i][1].y, cur[i][1].z, cur[i][1].w};
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                uint32_t p[4];
-                widen(w8[d], p);
-                const half8_t a = __builtin_bit_cast(half8_t, uint4{p[0], p[1], p[2], p[3]});
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh[i][d], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl[i][d], acc, 0, 0, 0);
-            }
-            if (gvalid[i]) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int n = tile * kMfmaRows + 4 * kg + e;
-                    const uint32_t smv = n < N ? sm[(int64_t)n * GK + g] : 0u;
-                    const float sf = f16_bits_to_f32(smv & 0xFFFFu), mf = f16_bits_to_f32(smv >> 16);
-                    part[e] = fmaf(sf * fsc[i], acc[e], part[e]);
-                    part[e] = fmaf(mf, xs[i], part[e]);
-                }
-            }
-        }
-        float *rb = red + (size_t)buf * W * 256;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rb[wave * 256 + (4 * kg + e) * 16 + j] = part[e];
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < kMfmaRows * M; idx += blockDim.x) {
-            const int r = idx / M, m = idx % M;
-            const int n = tile * kMfmaRows + r;
-            float v = 0.0f;
-            for (int w = 0; w < W; ++w) v += rb[w * 256 + r * 16 + m];
-            if (n < N) dst[(int64_t)m * N + n] = v;
-        }
-        buf ^= 1;
-#pragma unroll
-        for (int i = 0; i < GPW; ++i) {
-            cur[i][0] = nxt[i][0];
-            cur[i][1] = nxt[i][1];
+        for (int o = 1; o < 32; o <<= 1) delta += __shfl_xor(delta, o);
+        const int kg = c >> 1, d = (c & 1) * 4 + t;
+        *reinterpret_cast<uint4 *>(lds + (size_t)gl * kBGroupLds + ((d * 4 + kg) * kBRows + m) * 16) =
+            make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        if (sub == 0) {
+            fac[(gl * 3 + 0) * kBRows + m] = ldexpf(1.0f, 24 + sc);
+            fac[(gl * 3 + 1) * kBRows + m] = sum;
+            fac[(gl * 3 + 2) * kBRows + m] = 7.5f * delta;
         }
     }
 }
 
-// y[m][n] = sum over splits of partial[s][m][n], in split order
-__global__ __launch_bounds__(256) void k_splitk_sum(const float *__restrict__ partial,
-                                                    float *__restrict__ y, int64_t count, int nsplit)
+// Workgroup b covers K split b % nsplit and the b / nsplit-th of wps equal
+// ranges of 16-row units; its wave w takes units w, w + kBWaves, ... of that
+// range.  A wave streams (unit, group) items through a ring of D register
+// slots: each slot is refilled with the item D places later as soon as it is
+// consumed, so D items of weights stay in flight with no barrier in the loop.
+// Items past the wave's end load out of range (zeros) and write nothing.
+template <int D>
+__global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict__ x,
+                                                         const uint8_t *__restrict__ qs,
+                                                         const uint32_t *__restrict__ sm,
+                                                         float *__restrict__ out, int64_t ldo, int M,
+                                                         int N, int K, int gps, int nsplit, int wps)
 {
+    extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
+    const int lane = threadIdx.x & 63, j = lane & 15, kg = lane >> 4;
+    const int wave = threadIdx.x >> 6;
+    const int split = blockIdx.x % nsplit, wr = blockIdx.x / nsplit;
+    const int GK = K / kGroup;
+    const int g0 = split * gps;
+    const int gc = min(GK, g0 + gps) - g0;  // >= 1: the host makes every split non-empty
+    const int R = (N + kBRows - 1) / kBRows;
+    const int rb0 = (int)((int64_t)R * wr / wps), rb1 = (int)((int64_t)R * (wr + 1) / wps);
+    const int nunits = rb1 - rb0 > wave ? (rb1 - rb0 - wave + kBWaves - 1) / kBWaves : 0;
+    const int nitems = nunits * gc;
+    const uint32_t rowbytes = K / 2;
+    float *dst = out + (int64_t)split * M * ldo;  // partials: [split][M][ldo]
+
+    const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowbytes);
+    const rsrc_t r_sm = make_rsrc(sm, (uint32_t)N * GK * 4u);
+    uint4 wq[D][2];   // bytes 32kg..32kg+31 of group g of weight row 16 unit + j
+    uint32_t wsm[D];  // (scale, minimum) of that row and group
+    auto load_item = [&](int s, int unit, int gl) {
+        const bool ok = unit < nunits;
+        const int n = min((rb0 + wave + kBWaves * unit) * kBRows + j, N);  // row N reads zeros
+        const uint32_t o = ok ? (uint32_t)n * rowbytes + (uint32_t)(g0 + gl) * 128u + kg * 32 : 0x80000000u;
+        const uint32_t os = ok ? ((uint32_t)n * GK + g0 + gl) * 4u : 0x80000000u;
+        wq[s][0] = buf_load16(r_qs, o);
+        wq[s][1] = buf_load16(r_qs, o + 16);
+        wsm[s] = buf_load4(r_sm, os);
+    };
+    int lu = 0, lg = 0;  // next item to load
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+        load_item(s, lu, lg);
+        if (++lg == gc) { lg = 0; ++lu; }
+    }
+    fill_x_groups(x, M, K, g0, gc, xl);
+    __syncthreads();
+
+    const float *fac = reinterpret_cast<const float *>(xl + (size_t)gc * kBGroupLds);
+    float4_t yacc = {0.f, 0.f, 0.f, 0.f};
+    int cu = 0, cg = 0;  // item being computed
+    for (int base = 0; base < nitems; base += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            // the previous item's epilogue completes before this item's LDS
+            // reads are issued (only one item's operands are live at a time)
+            asm volatile("" : "+v"(yacc)::"memory");
+            const uint8_t *ag = xl + (size_t)cg * kBGroupLds + (kg * kBRows + j) * 16;
+            float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const half8_t a = *reinterpret_cast<const half8_t *>(ag + d * 4 * kBRows * 16);
+                const uint4 c4 = wq[s][d >> 2];
+                const uint32_t w = (d & 3) == 0 ? c4.x : (d & 3) == 1 ? c4.y : (d & 3) == 2 ? c4.z : c4.w;
+                uint32_t p[4];
+                widen(w, p);
+                const half8_t b = __builtin_bit_cast(half8_t, uint4{p[0], p[1], p[2], p[3]});
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+            }
+            const float4 f = *reinterpret_cast<const float4 *>(fac + (cg * 3 + 0) * kBRows + 4 * kg);
+            const float4 X = *reinterpret_cast<const float4 *>(fac + (cg * 3 + 1) * kBRows + 4 * kg);
+            const float4 cc = *reinterpret_cast<const float4 *>(fac + (cg * 3 + 2) * kBRows + 4 * kg);
+            const float sf = f16_bits_to_f32(wsm[s] & 0xFFFFu), mf = f16_bits_to_f32(wsm[s] >> 16);
+            yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
+            yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
+            yacc[2] = fmaf(sf, fmaf(f.z, acc[2], cc.z), fmaf(mf, X.z, yacc[2]));
+            yacc[3] = fmaf(sf, fmaf(f.w, acc[3], cc.w), fmaf(mf, X.w, yacc[3]));
+            if (cg == gc - 1) {
+                // unit complete: lane (j, kg) holds rows m = 4kg+e of column n
+                const int n = (rb0 + wave + kBWaves * cu) * kBRows + j;
+                if (cu < nunits && n < N) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * kg + e < M) dst[(int64_t)(4 * kg + e) * ldo + n] = yacc[e];
+                }
+                yacc = float4_t{0.f, 0.f, 0.f, 0.f};
+                cg = 0;
+                ++cu;
+            } else {
+                ++cg;
+            }
+            // slot s is consumed: refill it in place with the item D later
+            asm volatile("" : "+v"(yacc)::"memory");
+            load_item(s, lu, lg);
+            if (++lg == gc) { lg = 0; ++lu; }
+        }
+    }
+}
+
+// y[m][n] (row stride ldy) = sum over splits of partial[s][m][n] (dense
+// [nsplit][M][N]), in split order
+__global__ __launch_bounds__(256) void k_splitk_sum(const float *__restrict__ partial,
+                                                    float *__restrict__ y, int M, int N, int64_t ldy,
+                                                    int nsplit)
+{
+    const int64_t count = (int64_t)M * N;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
         float v = 0.0f;
         for (int s = 0; s < nsplit; ++s) v += partial[(int64_t)s * count + i];
-        y[i] = v;
+        y[(i / N) * ldy + i % N] = v;
     }
 }
 
-constexpr int kGpw = 2;         // groups of K per wave (B operands in registers)
-constexpr int kMaxWaves = 8;    // waves per workgroup
-
 struct MfmaCfg {
-    int waves, groups_per_split, nsplit, ntiles, grid;
-    size_t lds;
+    int nsplit, gps;
 };
 
-MfmaCfg choose_mfma(int64_t N, int K, const DeviceInfo &dev)
+// K split: as few splits as LDS allows, more while the 16-row units are too
+// few to give every wave of the chip one (small N), every split non-empty.
+// Independent of the device so the workspace size is too.
+MfmaCfg choose_mfma(int64_t N, int K)
 {
     MfmaCfg c{};
     const int GK = K / kGroup;
-    const int cap_groups = kGpw * kMaxWaves;
-    c.nsplit = (GK + cap_groups - 1) / cap_groups;
-    c.groups_per_split = (GK + c.nsplit - 1) / c.nsplit;
-    c.waves = (c.groups_per_split + kGpw - 1) / kGpw;
-    c.ntiles = (int)((N + kMfmaRows - 1) / kMfmaRows);
-    const int wgs_per_cu = 16 / c.waves > 0 ? 16 / c.waves : 1;
-    int64_t cap = (int64_t)dev.num_cus * wgs_per_cu;
-    cap = (cap + c.nsplit - 1) / c.nsplit;
-    c.grid = (int)(c.ntiles < cap ? c.ntiles : cap);
-    c.lds = (size_t)2 * c.waves * 256 * sizeof(float);
+    const int64_t R = (N + kBRows - 1) / kBRows;
+    int ns = (GK + kBMaxGroups - 1) / kBMaxGroups;
+    while (R * ns < kBTargetUnits && ns * 2 <= GK) ns *= 2;
+    c.gps = (GK + ns - 1) / ns;
+    c.nsplit = (GK + c.gps - 1) / c.gps;
     return c;
 }
 
@@ -483,39 +496,58 @@ MfmaCfg choose_mfma(int64_t N, int K, const DeviceInfo &dev)
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 1) return 0;
-    const int GK = (int)(K / kGroup);
-    const int nsplit = (GK + kGpw * kMaxWaves - 1) / (kGpw * kMaxWaves);
-    return nsplit > 1 ? (size_t)nsplit * M * N * sizeof(float) : 0;
+    const MfmaCfg c = choose_mfma(N, (int)K);
+    return c.nsplit > 1 ? (size_t)c.nsplit * M * N * sizeof(float) : 0;
 }
+
+static hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint16_t *sm,
+                                   int64_t N, int64_t ldy, int K, float *y, void *workspace,
+                                   const DeviceInfo &dev, hipStream_t stream);
 
 hipError_t launch_gemv(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
                        int K, float *y, void *workspace, const DeviceInfo &dev, hipStream_t stream)
 {
-    if (M == 1) {
-        // one descriptor addresses < 2 GiB of weights: split taller matrices
-        const int64_t rows_max = (kMaxBufferBytes - 1) / (K / 2);
-        for (int64_t n0 = 0; n0 < N; n0 += rows_max) {
-            const int64_t nn = N - n0 < rows_max ? N - n0 : rows_max;
-            const uint8_t *q = qs + n0 * (K / 2);
-            const uint16_t *s = sm + n0 * (K / kGroup) * 2;
-            const Dot2Cfg c = choose_dot2(nn, K, dev);
-            const hipError_t e = c.G == 16 ? dispatch_dot2<16>(c, x, q, s, nn, K, y + n0, stream)
-                                           : dispatch_dot2<8>(c, x, q, s, nn, K, y + n0, stream);
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
+    // one descriptor addresses < 2 GiB of weights: split taller matrices into
+    // row ranges (y keeps its row stride N)
+    const int64_t rows_max = ((kMaxBufferBytes - 1) / (K / 2)) / 64 * 64;
+    for (int64_t n0 = 0; n0 < N; n0 += rows_max) {
+        const int64_t nn = N - n0 < rows_max ? N - n0 : rows_max;
+        const hipError_t e = launch_gemv_rows(x, M, qs + n0 * (K / 2), sm + n0 * (K / kGroup) * 2, nn,
+                                              N, K, y + n0, workspace, dev, stream);
+        if (e != hipSuccess) return e;
     }
-    const MfmaCfg c = choose_mfma(N, K, dev);
+    return hipSuccess;
+}
+
+static hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint16_t *sm,
+                                   int64_t N, int64_t ldy, int K, float *y, void *workspace,
+                                   const DeviceInfo &dev, hipStream_t stream)
+{
+    if (M == 1) {
+        const Dot2Cfg c = choose_dot2(N, K, dev);
+        return c.G == 16 ? dispatch_dot2<16>(c, x, qs, sm, N, K, y, stream)
+                         : dispatch_dot2<8>(c, x, qs, sm, N, K, y, stream);
+    }
+    const MfmaCfg c = choose_mfma(N, K);
+    const size_t lds = arm_b_lds_bytes(c.gps);
+    if (lds > (size_t)dev.lds_bytes) return hipErrorInvalidConfiguration;
+    const int64_t R = (N + kBRows - 1) / kBRows;
+    // workgroups per split: one per CU overall, at most one per kBWaves units
+    int64_t wps = dev.num_cus / c.nsplit;
+    if (wps < 1) wps = 1;
+    if (wps > (R + kBWaves - 1) / kBWaves) wps = (R + kBWaves - 1) / kBWaves;
+    // split-K partials are dense [nsplit][M][N]; otherwise y is written directly
     float *out = c.nsplit > 1 ? static_cast<float *>(workspace) : y;
-    hipLaunchKernelGGL((k_gemv_mfma<kGpw>), dim3(c.grid, c.nsplit), dim3(kWave * c.waves), c.lds,
-                       stream, x, qs, reinterpret_cast<const uint32_t *>(sm), out, M, (int)N, K,
-                       c.groups_per_split, c.ntiles);
+    const int64_t ldo = c.nsplit > 1 ? N : ldy;
+    hipLaunchKernelGGL((k_gemv_mfma<kBDepth>), dim3((unsigned)(wps * c.nsplit)), dim3(kBThreads), lds,
+                       stream, x, qs, reinterpret_cast<const uint32_t *>(sm), out, ldo, M, (int)N, K,
+                       c.gps, c.nsplit, (int)wps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.nsplit == 1) return e;
     const int64_t count = (int64_t)M * N;
-    int64_t blocks = (count + 255) / 256;
-    if (blocks > (int64_t)dev.num_cus * 8) blocks = (int64_t)dev.num_cus * 8;
-    hipLaunchKernelGGL(k_splitk_sum, dim3((unsigned)blocks), dim3(256), 0, stream, out, y, count,
+    int64_t sb = (count + 255) / 256;
+    if (sb > (int64_t)dev.num_cus * 8) sb = (int64_t)dev.num_cus * 8;
+    hipLaunchKernelGGL(k_splitk_sum, dim3((unsigned)sb), dim3(256), 0, stream, out, y, M, (int)N, ldy,
                        c.nsplit);
     return hipGetLastError();
 }

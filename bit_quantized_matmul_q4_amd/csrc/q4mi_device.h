@@ -23,6 +23,7 @@ constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowRor8 = 0x128;     // row_ror:8 (rotate right by 8 within 16 lanes)
 
 template <int ctrl>
 __device__ __forceinline__ float dpp_f32(float v)
