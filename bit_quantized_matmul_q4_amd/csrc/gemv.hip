@@ -1,7 +1,7 @@
 // gemv.hip -- dequant-fused GEMV for decode: y[m][n] = sum_k x[m][k] * w[n][k]
 // with 4-bit group-256 weights, 1..16 fp32 activation rows, fp32 output (the
-// "tiny-N f32-out GEMV" and "split-K" arms of the decode work on the llama.cpp
-// / hipfire pages, "Starting position"), designed for gfx950.  It is bound by
+// "tiny-N f32-out GEMV" and "split-K GEMM" arms of the vllm.cpp issue
+// "GFX1100-TG200", section "Starting position"), designed for gfx950.  It is bound by
 // HBM: every weight byte is read once (0.516 B per weight), so the kernels are
 // built around coalesced 16-byte buffer loads kept in flight in register rings.
 //
@@ -9,8 +9,8 @@
 //   * Nibble widening by masking alone.  A dword of qs holds 8 codes; masking
 //     it with 0x000F000F or 0x00F000F0 leaves two codes in the mantissas of two
 //     fp16 halves, i.e. the exact fp16 subnormals q * 2^-24 and q * 2^-20
-//     (the same idea as the gfx942 KV-cache page, "Design choices", where one
-//     v_perm makes each code byte an exact fp16 subnormal).  Activations paired
+//     (the same idea as the vLLM "ROCM_OCTAVE" KV-cache pull request, "Design
+//     choices", where one v_perm makes each code byte an exact fp16 subnormal).  Activations paired
 //     with the high nibbles are stored pre-multiplied by 2^-4, so both land on
 //     one scale.
 //   * Activations become fp16 after scaling a chunk (arm A: 32 elements) or a
