@@ -82,16 +82,35 @@ __device__ __forceinline__ int chunk_exp(float amax)
 // 80-byte stride puts 16-byte reads of consecutive chunks by consecutive lanes
 // on distinct LDS banks.
 constexpr int kChunkLds = 80;
+// activation items per thread whose loads go out ahead of the weight loads
+constexpr int kFillRegs = 2;
 
-// Four threads per chunk; thread i converts dword i of it (elements 4i..4i+3
-// and 16+4i..16+4i+3).  C is a multiple of 8 and blockDim a multiple of 64,
-// so the four threads of a chunk are always active together.
-__device__ __forceinline__ void fill_x_chunks(const float *__restrict__ x, int C, uint8_t *lds)
+// Item idx = (chunk c, dword i) of the image needs x[32c+4i..+3] (low nibbles)
+// and x[32c+16+4i..+3] (high nibbles).  Thread t takes items base + t + it *
+// blockDim.x; items past the end read zeros and are not stored.
+struct XItems {
+    float4 a[kFillRegs], b[kFillRegs];
+};
+
+__device__ __forceinline__ void load_x_items(rsrc_t rx, int C, int base, XItems &v)
 {
-    for (int idx = threadIdx.x; idx < C * 4; idx += blockDim.x) {
-        const int c = idx >> 2, i = idx & 3;
-        const float4 a = *reinterpret_cast<const float4 *>(x + c * 32 + 4 * i);
-        const float4 b = *reinterpret_cast<const float4 *>(x + c * 32 + 16 + 4 * i);
+#pragma unroll
+    for (int it = 0; it < kFillRegs; ++it) {
+        const int idx = base + threadIdx.x + it * blockDim.x;
+        const uint32_t off = idx < C * 4 ? (uint32_t)((idx >> 2) * 32 + 4 * (idx & 3)) * 4u : 0x80000000u;
+        v.a[it] = __builtin_bit_cast(float4, buf_load16(rx, off));
+        v.b[it] = __builtin_bit_cast(float4, buf_load16(rx, off + 64));
+    }
+}
+
+// Four consecutive threads hold the four dwords of one chunk (blockDim is a
+// multiple of 64, so they are active together).
+__device__ __forceinline__ void convert_x_items(int C, int base, const XItems &v, uint8_t *lds)
+{
+#pragma unroll
+    for (int it = 0; it < kFillRegs; ++it) {
+        const int idx = base + threadIdx.x + it * blockDim.x;
+        const float4 a = v.a[it], b = v.b[it];
         float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                            fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
         float sum = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
@@ -102,135 +121,173 @@ __device__ __forceinline__ void fill_x_chunks(const float *__restrict__ x, int C
         const int sc = chunk_exp(amax);
         const float ls = ldexpf(1.0f, -sc), hs = ldexpf(1.0f, -sc - 4);
         // pairs of dword i: (4i, 4i+2) (16+4i, 16+4i+2) (4i+1, 4i+3) (16+4i+1, 16+4i+3)
-        const float v[8] = {a.x * ls, a.z * ls, b.x * hs, b.z * hs, a.y * ls, a.w * ls, b.y * hs, b.w * hs};
+        const float w[8] = {a.x * ls, a.z * ls, b.x * hs, b.z * hs, a.y * ls, a.w * ls, b.y * hs, b.w * hs};
         uint32_t hw[4];
         float dl = 0.0f, dh = 0.0f;  // residuals of low / high slots, in scaled units
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const _Float16 h0 = (_Float16)v[2 * p], h1 = (_Float16)v[2 * p + 1];
-            const float r = (v[2 * p] - (float)h0) + (v[2 * p + 1] - (float)h1);
+            const _Float16 h0 = (_Float16)w[2 * p], h1 = (_Float16)w[2 * p + 1];
+            const float r = (w[2 * p] - (float)h0) + (w[2 * p + 1] - (float)h1);
             if (p & 1) dh += r; else dl += r;
             hw[p] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
         }
         float delta = ldexpf(dl, sc) + ldexpf(dh, sc + 4);
         delta += __shfl_xor(delta, 1);
         delta += __shfl_xor(delta, 2);
-        uint8_t *dst = lds + c * kChunkLds;
-        *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        if (i == 0)
-            *reinterpret_cast<float4 *>(dst + 64) = make_float4(ldexpf(1.0f, 24 + sc), sum, 7.5f * delta, 0.0f);
+        if (idx < C * 4) {
+            uint8_t *dst = lds + (idx >> 2) * kChunkLds;
+            const int i = idx & 3;
+            *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            if (i == 0)
+                *reinterpret_cast<float4 *>(dst + 64) = make_float4(ldexpf(1.0f, 24 + sc), sum, 7.5f * delta, 0.0f);
+        }
     }
 }
 
-// Work of one wave: "batches" of RB = (64/G)*U consecutive rows.  A batch is
-// covered in P passes of CB chunks per lane (lane j of a row owns chunks
-// j + G*t, t < CB*P, so every chunk of the row once).  The registers of each
-// (row step u, chunk t) are refilled with the next pass's data as soon as they
-// are consumed, which keeps about U*CB*16 bytes per lane in flight.
+// A workgroup has B x S waves: wave w works on K slice s = w % S of row batch
+// w / S.  A batch is RB = (64/G)*U rows; lane j of a row owns the 16-byte
+// chunks j + G*t.  Slice s of a row covers chunk steps [s*P*CB, (s+1)*P*CB),
+// taken in P passes of CB chunks; the registers of each (row step u, chunk t)
+// are refilled with the next pass (or the next round's batch) as soon as they
+// are consumed.  The activation loads go out first, the weight loads next, so
+// the fp16 image is built while the weights are in flight.  Row partials are
+// summed over the G lanes with DPP and, with S > 1, over the slices through
+// LDS in slice order.  All waves run the same number of rounds (batches past
+// the end read zeros), so the slice barriers are uniform.
 template <int CB, int U, int G>
-__global__ __launch_bounds__(256) void k_gemv_dot2(const float *__restrict__ x,
-                                                   const uint8_t *__restrict__ qs,
-                                                   const uint32_t *__restrict__ sm,
-                                                   float *__restrict__ y, int N, int K, int P,
-                                                   int nbatches)
+__global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
+                                                    const uint8_t *__restrict__ qs,
+                                                    const uint32_t *__restrict__ sm,
+                                                    float *__restrict__ y, int N, int K, int S, int P,
+                                                    int rounds)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     constexpr int RPW = kWave / G;
     constexpr int RB = RPW * U;
     const int lane = threadIdx.x & 63, j = lane % G, rq = lane / G;
+    const int wave = threadIdx.x >> 6;
+    const int s = wave % S, bi = wave / S, B = (blockDim.x >> 6) / S;
     const int C = K / 32, gpr = K / kGroup;
-    const int64_t rowbytes = K / 2;
-    const int W = gridDim.x * (blockDim.x / kWave);
-    const int wb = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+    const uint32_t rowbytes = K / 2;
+    const int bstride = gridDim.x * B;
 
-    const rsrc_t rq_qs = make_rsrc(qs, (uint32_t)(N * rowbytes));
-    const rsrc_t rq_sm = make_rsrc(sm, (uint32_t)N * gpr * 4u);
+    const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowbytes);
+    const rsrc_t r_sm = make_rsrc(sm, (uint32_t)N * gpr * 4u);
+    const rsrc_t r_x = make_rsrc(x, (uint32_t)K * 4u);
     uint4 q[U][CB];
     uint32_t smv[U][CB];
-    // rows past the end (including every row of a batch past the last) read
-    // as zeros through the descriptor bounds
+    // rows past the end (every row of a batch past the last) read zeros
     auto load_item = [&](int b, int pass, int u, int t) {
         const int n = min(b * RB + u * RPW + rq, N);
-        const int c = j + G * (pass * CB + t);
-        q[u][t] = buf_load16(rq_qs, (uint32_t)n * (uint32_t)rowbytes + c * 16);
-        smv[u][t] = buf_load4(rq_sm, ((uint32_t)n * gpr + (c >> 3)) * 4u);
+        const int c = j + G * ((s * P + pass) * CB + t);
+        q[u][t] = buf_load16(r_qs, (uint32_t)n * rowbytes + c * 16);
+        smv[u][t] = buf_load4(r_sm, ((uint32_t)n * gpr + (c >> 3)) * 4u);
     };
-    // first item's loads go out before the activation fill
+    XItems xv;
+    load_x_items(r_x, C, 0, xv);
+    int b = blockIdx.x * B + bi;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int t = 0; t < CB; ++t) load_item(wb, 0, u, t);
-    fill_x_chunks(x, C, xl);
+        for (int t = 0; t < CB; ++t) load_item(b, 0, u, t);
+    convert_x_items(C, 0, xv, xl);
+    for (int base = kFillRegs * blockDim.x; base < C * 4; base += kFillRegs * blockDim.x) {
+        load_x_items(r_x, C, base, xv);
+        convert_x_items(C, base, xv, xl);
+    }
     __syncthreads();
+    float *red = reinterpret_cast<float *>(xl + C * kChunkLds);  // [B][S][RB] slice partials
 
     float p[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) p[u] = 0.0f;
-    int b = wb, pass = 0;
-    while (b < nbatches) {
-        int nb = b, np = pass + 1;
-        if (np == P) { np = 0; nb = b + W; }
+    for (int r = 0; r < rounds; ++r) {
+        const int nb = b + bstride;  // past the end in the last round: zeros
+        for (int pass = 0; pass < P; ++pass) {
+            const int lb = pass + 1 < P ? b : nb, lp = pass + 1 < P ? pass + 1 : 0;
 #pragma unroll
-        for (int t = 0; t < CB; ++t) {
-            // The partial sums of chunk t-1 must exist before chunk t's
-            // activation reads are issued: only one chunk's 16 activation
-            // registers are live, and the loads refilled below stay in flight.
+            for (int t = 0; t < CB; ++t) {
+                // The partial sums of chunk t-1 must exist before chunk t's
+                // activation reads are issued: only one chunk's 16 activation
+                // registers are live, and the loads refilled below stay in flight.
 #pragma unroll
-            for (int u = 0; u < U; ++u) asm volatile("" : "+v"(p[u])::"memory");
-            const int c = j + G * (pass * CB + t);
-            const uint8_t *xc = xl + c * kChunkLds;
-            uint4 hv[4];
+                for (int u = 0; u < U; ++u) asm volatile("" : "+v"(p[u])::"memory");
+                const int c = j + G * ((s * P + pass) * CB + t);
+                const uint8_t *xc = xl + c * kChunkLds;
+                uint4 hv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hv[i] = *reinterpret_cast<const uint4 *>(xc + 16 * i);
-            const float4 fx = *reinterpret_cast<const float4 *>(xc + 64);
-            const uint32_t xh[16] = {hv[0].x, hv[0].y, hv[0].z, hv[0].w, hv[1].x, hv[1].y, hv[1].z, hv[1].w,
-                                     hv[2].x, hv[2].y, hv[2].z, hv[2].w, hv[3].x, hv[3].y, hv[3].z, hv[3].w};
+                for (int i = 0; i < 4; ++i) hv[i] = *reinterpret_cast<const uint4 *>(xc + 16 * i);
+                const float4 fx = *reinterpret_cast<const float4 *>(xc + 64);
+                const uint32_t xh[16] = {hv[0].x, hv[0].y, hv[0].z, hv[0].w, hv[1].x, hv[1].y, hv[1].z, hv[1].w,
+                                         hv[2].x, hv[2].y, hv[2].z, hv[2].w, hv[3].x, hv[3].y, hv[3].z, hv[3].w};
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float acc = 0.0f;
-                const uint32_t w4[4] = {q[u][t].x, q[u][t].y, q[u][t].z, q[u][t].w};
+                for (int u = 0; u < U; ++u) {
+                    float acc = 0.0f;
+                    const uint32_t w4[4] = {q[u][t].x, q[u][t].y, q[u][t].z, q[u][t].w};
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    uint32_t pw[4];
-                    widen(w4[d], pw);
+                    for (int d = 0; d < 4; ++d) {
+                        uint32_t pw[4];
+                        widen(w4[d], pw);
 #pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        acc = __builtin_amdgcn_fdot2(as_half2(pw[k]), as_half2(xh[4 * d + k]), acc, false);
+                        for (int k = 0; k < 4; ++k)
+                            acc = __builtin_amdgcn_fdot2(as_half2(pw[k]), as_half2(xh[4 * d + k]), acc, false);
+                    }
+                    const uint32_t sv = smv[u][t];
+                    const float sf = f16_bits_to_f32(sv & 0xFFFFu), mf = f16_bits_to_f32(sv >> 16);
+                    p[u] = fmaf(sf, fmaf(fx.x, acc, fx.z), fmaf(mf, fx.y, p[u]));
                 }
-                const uint32_t sv = smv[u][t];
-                const float sf = f16_bits_to_f32(sv & 0xFFFFu), mf = f16_bits_to_f32(sv >> 16);
-                p[u] = fmaf(sf, fmaf(fx.x, acc, fx.z), fmaf(mf, fx.y, p[u]));
+                // registers of chunk t are consumed: refill them in place (the
+                // fence keeps the loads below the compute, so the loaded
+                // registers are the loop-carried ones and need no copy)
+#pragma unroll
+                for (int u = 0; u < U; ++u) asm volatile("" : "+v"(p[u])::"memory");
+#pragma unroll
+                for (int u = 0; u < U; ++u) load_item(lb, lp, u, t);
             }
-            // registers of chunk t are consumed: refill them in place with the
-            // next item (the fence keeps the loads below the compute, so the
-            // loaded registers are the loop-carried ones and need no copy)
-#pragma unroll
-            for (int u = 0; u < U; ++u) asm volatile("" : "+v"(p[u])::"memory");
-#pragma unroll
-            for (int u = 0; u < U; ++u) load_item(nb, np, u, t);
         }
-        if (np == 0) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float v = group_sum<G>(p[u]);
-                const int n = b * RB + u * RPW + rq;
+        for (int u = 0; u < U; ++u) {
+            const float v = group_sum<G>(p[u]);
+            p[u] = 0.0f;
+            const int n = b * RB + u * RPW + rq;
+            if (S == 1) {
                 if (j == 0 && n < N) y[n] = v;
-                p[u] = 0.0f;
+            } else if (j == 0) {
+                red[(bi * S + s) * RB + u * RPW + rq] = v;
             }
+        }
+        if (S > 1) {
+            __syncthreads();
+            if (s == 0 && j == 0) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float v = 0.0f;
+                    for (int k = 0; k < S; ++k) v += red[(bi * S + k) * RB + u * RPW + rq];
+                    const int n = b * RB + u * RPW + rq;
+                    if (n < N) y[n] = v;
+                }
+            }
+            __syncthreads();
         }
         b = nb;
-        pass = np;
     }
 }
 
-// row steps U per chunk-block size CB: about 8-10 loads of 16 B in flight per lane
+// row steps U per chunk-block size CB in the persistent mode: about 8-10 loads
+// of 16 B in flight per lane
 constexpr int kRowStepsFor[9] = {0, 8, 4, 2, 2, 1, 1, 1, 1};
 
 struct Dot2Cfg {
-    int G, CB, U, P, nbatches, grid;
+    int G, CB, U, S, P, B, rounds, grid;
     size_t lds;
 };
 
+// Two modes.  Small N (up to about 12 row batches per CU): one round in which
+// every wave makes a single pass, CB the largest chunk block dividing the
+// lane's chunks and K split over S = chunks / CB waves; four batches per
+// workgroup, which amortises the activation image over 4 S waves, or one
+// batch per workgroup when that leaves fewer workgroups than half the CUs.
+// Large N: persistent waves (S = 1), every wave the same number of batches.
 Dot2Cfg choose_dot2(int64_t N, int K, const DeviceInfo &dev)
 {
     Dot2Cfg c{};
@@ -238,45 +295,85 @@ Dot2Cfg choose_dot2(int64_t N, int K, const DeviceInfo &dev)
     c.G = (C % 16 == 0) ? 16 : 8;
     const int cpt = C / c.G;  // chunks per lane per row
     static const int cbs[] = {8, 6, 5, 4, 3, 2, 1};
+    const int rpw = kWave / c.G;
+    const int64_t nb1 = (N + rpw - 1) / rpw;  // batches at U = 1
     c.CB = 1;
     for (int cb : cbs)
         if (cpt % cb == 0) { c.CB = cb; break; }
-    c.P = cpt / c.CB;
-    c.U = kRowStepsFor[c.CB];
-    const int rb = (kWave / c.G) * c.U;
-    c.nbatches = (int)((N + rb - 1) / rb);
-    // persistent waves, at most 6 workgroups of 4 waves per CU; every wave
-    // gets the same number of batches (rounds) so no round runs half empty
-    const int waves_per_wg = 4;
-    const int64_t max_waves = (int64_t)dev.num_cus * 6 * waves_per_wg;
-    const int64_t rounds = (c.nbatches + max_waves - 1) / max_waves;
-    const int64_t waves = (c.nbatches + rounds - 1) / rounds;
-    c.grid = (int)((waves + waves_per_wg - 1) / waves_per_wg);
-    c.lds = (size_t)C * kChunkLds;
+    if (nb1 <= (int64_t)dev.num_cus * 12) {
+        c.U = 1;
+        c.B = 4;
+        if ((nb1 + c.B - 1) / c.B < dev.num_cus / 2) {
+            c.B = 1;
+            c.CB = 1;
+        }
+        // slices: the largest divisor of the chunk steps that fits 16 / B waves
+        const int m = cpt / c.CB;
+        c.S = 1;
+        for (int sl = 1; sl <= m && sl * c.B <= 16; ++sl)
+            if (m % sl == 0) c.S = sl;
+        c.P = m / c.S;
+        c.rounds = 1;
+        c.grid = (int)((nb1 + c.B - 1) / c.B);
+    } else {
+        c.U = kRowStepsFor[c.CB];
+        c.S = 1;
+        c.P = cpt / c.CB;
+        c.B = 4;
+        c.rounds = 0;  // set at launch from the kernel's occupancy
+    }
+    c.lds = (size_t)C * kChunkLds + (size_t)c.B * c.S * rpw * c.U * sizeof(float);
     return c;
 }
 
 template <int CB, int U, int G>
-hipError_t run_dot2(const Dot2Cfg &c, const float *x, const uint8_t *qs, const uint16_t *sm,
-                    int64_t N, int K, float *y, hipStream_t stream)
+hipError_t run_dot2(Dot2Cfg c, const float *x, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                    int K, float *y, const DeviceInfo &dev, hipStream_t stream)
 {
-    hipLaunchKernelGGL((k_gemv_dot2<CB, U, G>), dim3(c.grid), dim3(256), c.lds, stream, x, qs,
-                       reinterpret_cast<const uint32_t *>(sm), y, (int)N, K, c.P, c.nbatches);
+    const auto kernel = k_gemv_dot2<CB, U, G>;
+    if (c.rounds == 0) {
+        // persistent: as many workgroups as fit on the chip at once, every wave
+        // the same number of row batches (rounds) so no round runs half empty
+        // (a host-side query of the kernel's register and LDS needs; only
+        // large launches take this path)
+        int wgs_per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs_per_cu, reinterpret_cast<const void *>(kernel),
+                                                         kWave * c.B * c.S, c.lds) != hipSuccess ||
+            wgs_per_cu < 1)
+            wgs_per_cu = 1;
+        const int64_t rb = (int64_t)(kWave / G) * U;
+        const int64_t nbatches = (N + rb - 1) / rb;
+        const int64_t max_waves = (int64_t)dev.num_cus * wgs_per_cu * c.B;
+        c.rounds = (int)((nbatches + max_waves - 1) / max_waves);
+        const int64_t waves = (nbatches + c.rounds - 1) / c.rounds;
+        c.grid = (int)((waves + c.B - 1) / c.B);
+    }
+    hipLaunchKernelGGL(kernel, dim3(c.grid), dim3(kWave * c.B * c.S), c.lds, stream, x, qs,
+                       reinterpret_cast<const uint32_t *>(sm), y, (int)N, K, c.S, c.P, c.rounds);
     return hipGetLastError();
 }
 
 template <int G>
 hipError_t dispatch_dot2(const Dot2Cfg &c, const float *x, const uint8_t *qs, const uint16_t *sm,
-                         int64_t N, int K, float *y, hipStream_t stream)
+                         int64_t N, int K, float *y, const DeviceInfo &dev, hipStream_t stream)
 {
-    switch (c.CB) {
-    case 1: return run_dot2<1, kRowStepsFor[1], G>(c, x, qs, sm, N, K, y, stream);
-    case 2: return run_dot2<2, kRowStepsFor[2], G>(c, x, qs, sm, N, K, y, stream);
-    case 3: return run_dot2<3, kRowStepsFor[3], G>(c, x, qs, sm, N, K, y, stream);
-    case 4: return run_dot2<4, kRowStepsFor[4], G>(c, x, qs, sm, N, K, y, stream);
-    case 5: return run_dot2<5, kRowStepsFor[5], G>(c, x, qs, sm, N, K, y, stream);
-    case 6: return run_dot2<6, kRowStepsFor[6], G>(c, x, qs, sm, N, K, y, stream);
-    case 8: return run_dot2<8, kRowStepsFor[8], G>(c, x, qs, sm, N, K, y, stream);
+    if (c.U == 1) {
+        switch (c.CB) {
+        case 1: return run_dot2<1, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 2: return run_dot2<2, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 3: return run_dot2<3, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 4: return run_dot2<4, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 5: return run_dot2<5, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 6: return run_dot2<6, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 8: return run_dot2<8, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
+        }
+    } else {
+        switch (c.CB) {
+        case 1: return run_dot2<1, kRowStepsFor[1], G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 2: return run_dot2<2, kRowStepsFor[2], G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 3: return run_dot2<3, kRowStepsFor[3], G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 4: return run_dot2<4, kRowStepsFor[4], G>(c, x, qs, sm, N, K, y, dev, stream);
+        }
     }
     return hipErrorInvalidValue;
 }
@@ -525,8 +622,8 @@ static hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, con
 {
     if (M == 1) {
         const Dot2Cfg c = choose_dot2(N, K, dev);
-        return c.G == 16 ? dispatch_dot2<16>(c, x, qs, sm, N, K, y, stream)
-                         : dispatch_dot2<8>(c, x, qs, sm, N, K, y, stream);
+        return c.G == 16 ? dispatch_dot2<16>(c, x, qs, sm, N, K, y, dev, stream)
+                         : dispatch_dot2<8>(c, x, qs, sm, N, K, y, dev, stream);
     }
     const MfmaCfg c = choose_mfma(N, K);
     const size_t lds = arm_b_lds_bytes(c.gps);
