@@ -165,7 +165,7 @@ __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
     constexpr int RPW = kWave / G;
     constexpr int RB = RPW * U;
     const int lane = threadIdx.x & 63, j = lane % G, rq = lane / G;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s = wave % S, bi = wave / S, B = (blockDim.x >> 6) / S;
     const int C = K / 32, gpr = K / kGroup;
     const uint32_t rowbytes = K / 2;
@@ -180,8 +180,8 @@ __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
     auto load_item = [&](int b, int pass, int u, int t) {
         const int n = min(b * RB + u * RPW + rq, N);
         const int c = j + G * ((s * P + pass) * CB + t);
-        q[u][t] = buf_load16(r_qs, (uint32_t)n * rowbytes + c * 16);
-        smv[u][t] = buf_load4(r_sm, ((uint32_t)n * gpr + (c >> 3)) * 4u);
+        q[u][t] = buf_load16_nt(r_qs, (uint32_t)n * rowbytes + c * 16);
+        smv[u][t] = buf_load4_nt(r_sm, ((uint32_t)n * gpr + (c >> 3)) * 4u);
     };
     XItems xv;
     load_x_items(r_x, C, 0, xv);
@@ -389,13 +389,15 @@ hipError_t dispatch_dot2(const Dot2Cfg &c, const float *x, const uint8_t *qs, co
 constexpr int kBRows = 16;                      // weight rows per unit (one MFMA column block)
 constexpr int kBWaves = 8;                      // waves per workgroup
 constexpr int kBThreads = kBWaves * kWave;
-constexpr int kBMaxGroups = 18;                 // K groups one workgroup holds in LDS
+constexpr int kBMaxGroups = 16;                 // K groups one workgroup holds in LDS
 constexpr int kBGroupLds = 8 * 4 * kBRows * 16; // A image of one group: [step 8][kg 4][m 16] x 16 B
 constexpr int kBFacLds = 3 * kBRows * 4;        // per group: f[16], X[16], c[16] (fp32)
 constexpr int kBDepth = 12;                     // (unit, group) items in flight per wave
 constexpr int kBTargetUnits = 256 * kBWaves;    // units wanted before K is split further
 
-__host__ __device__ constexpr size_t arm_b_lds_bytes(int gps) { return (size_t)gps * (kBGroupLds + kBFacLds); }
+__host__ __device__ constexpr size_t arm_b_x_lds_bytes(int gps) { return (size_t)gps * (kBGroupLds + kBFacLds); }
+// activation image plus one weight transposition tile per wave (16 rows x 144 B)
+__host__ __device__ constexpr size_t arm_b_lds_bytes(int gps) { return arm_b_x_lds_bytes(gps) + kBWaves * 16 * 144; }
 
 // Activations of groups g0 .. g0+gc-1 into LDS.  32 threads per (row m, group):
 // thread (c, t) converts dword t of chunk c, i.e. elements 32c+4t..32c+4t+3
@@ -404,21 +406,42 @@ __host__ __device__ constexpr size_t arm_b_lds_bytes(int gps) { return (size_t)g
 // f = 2^(24+e) that undoes the group's power-of-two scaling and the subnormal
 // weights, X = sum of x, and c = 7.5 * sum of (x - hi): the codes' mean share
 // of the fp16 rounding of x, folded back in exactly (the remaining error is
-// sum (x - hi) (q - 7.5), with centred codes).
-__device__ __forceinline__ void fill_x_groups(const float *__restrict__ x, int M, int K, int g0, int gc,
-                                              uint8_t *lds)
+// sum (x - hi) (q - 7.5), with centred codes).  Items are taken kXBatch per
+// thread at a time, all their loads issued before any is used; rows >= M and
+// items past the end read zeros (buffer bounds).
+constexpr int kXBatch = 8;
+
+struct XGroupItems {
+    float4 a[kXBatch], b[kXBatch];
+};
+
+__device__ __forceinline__ void load_x_groups(rsrc_t rx, int M, int K, int g0, int gc, int base,
+                                              XGroupItems &v)
 {
-    float *fac = reinterpret_cast<float *>(lds + (size_t)gc * kBGroupLds);
-    for (int idx = threadIdx.x; idx < kBRows * gc * 32; idx += blockDim.x) {
+#pragma unroll
+    for (int it = 0; it < kXBatch; ++it) {
+        const int idx = base + threadIdx.x + it * blockDim.x;
         const int pair = idx >> 5, sub = idx & 31;
         const int m = pair & (kBRows - 1), gl = pair >> 4;
         const int c = sub >> 2, t = sub & 3;
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (m < M) {
-            const float *xp = x + (int64_t)m * K + (int64_t)(g0 + gl) * kGroup + c * 32;
-            a = *reinterpret_cast<const float4 *>(xp + 4 * t);
-            b = *reinterpret_cast<const float4 *>(xp + 16 + 4 * t);
-        }
+        const bool ok = m < M && gl < gc;
+        const uint32_t off =
+            ok ? (uint32_t)(m * K + (g0 + gl) * kGroup + c * 32 + 4 * t) * 4u : 0x80000000u;
+        v.a[it] = __builtin_bit_cast(float4, buf_load16(rx, off));
+        v.b[it] = __builtin_bit_cast(float4, buf_load16(rx, off + 64));
+    }
+}
+
+__device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupItems &v, uint8_t *lds)
+{
+    float *fac = reinterpret_cast<float *>(lds + (size_t)gc * kBGroupLds);
+#pragma unroll
+    for (int it = 0; it < kXBatch; ++it) {
+        const int idx = base + threadIdx.x + it * blockDim.x;
+        const int pair = idx >> 5, sub = idx & 31;
+        const int m = pair & (kBRows - 1), gl = pair >> 4;
+        const int c = sub >> 2, t = sub & 3;
+        const float4 a = v.a[it], b = v.b[it];
         float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                            fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
         float sum = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
@@ -430,77 +453,112 @@ __device__ __forceinline__ void fill_x_groups(const float *__restrict__ x, int M
         const int sc = chunk_exp(amax);
         const float ls = ldexpf(1.0f, -sc), hs = ldexpf(1.0f, -sc - 4);
         // slot order of one widened dword: (4t, 4t+2) (16+4t, 16+4t+2) (4t+1, 4t+3) (16+4t+1, 16+4t+3)
-        const float v[8] = {a.x * ls, a.z * ls, b.x * hs, b.z * hs, a.y * ls, a.w * ls, b.y * hs, b.w * hs};
+        const float w[8] = {a.x * ls, a.z * ls, b.x * hs, b.z * hs, a.y * ls, a.w * ls, b.y * hs, b.w * hs};
         uint32_t hw[4];
         float dl = 0.0f, dh = 0.0f;  // residuals of low / high slots, in scaled units
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const _Float16 h0 = (_Float16)v[2 * p], h1 = (_Float16)v[2 * p + 1];
-            const float r = (v[2 * p] - (float)h0) + (v[2 * p + 1] - (float)h1);
+            const _Float16 h0 = (_Float16)w[2 * p], h1 = (_Float16)w[2 * p + 1];
+            const float r = (w[2 * p] - (float)h0) + (w[2 * p + 1] - (float)h1);
             if (p & 1) dh += r; else dl += r;
             hw[p] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
         }
         float delta = ldexpf(dl, sc) + ldexpf(dh, sc + 4);
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) delta += __shfl_xor(delta, o);
-        const int kg = c >> 1, d = (c & 1) * 4 + t;
-        *reinterpret_cast<uint4 *>(lds + (size_t)gl * kBGroupLds + ((d * 4 + kg) * kBRows + m) * 16) =
-            make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        if (sub == 0) {
-            fac[(gl * 3 + 0) * kBRows + m] = ldexpf(1.0f, 24 + sc);
-            fac[(gl * 3 + 1) * kBRows + m] = sum;
-            fac[(gl * 3 + 2) * kBRows + m] = 7.5f * delta;
+        if (gl < gc) {
+            const int kg = c & 3, d = (c >> 2) * 4 + t;
+            *reinterpret_cast<uint4 *>(lds + (size_t)gl * kBGroupLds + ((d * 4 + kg) * kBRows + m) * 16) =
+                make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            if (sub == 0) {
+                fac[(gl * 3 + 0) * kBRows + m] = ldexpf(1.0f, 24 + sc);
+                fac[(gl * 3 + 1) * kBRows + m] = sum;
+                fac[(gl * 3 + 2) * kBRows + m] = 7.5f * delta;
+            }
         }
     }
 }
 
-// Workgroup b covers K split b % nsplit and the b / nsplit-th of wps equal
-// ranges of 16-row units; its wave w takes units w, w + kBWaves, ... of that
-// range.  A wave streams (unit, group) items through a ring of D register
-// slots: each slot is refilled with the item D places later as soon as it is
-// consumed, so D items of weights stay in flight with no barrier in the loop.
-// Items past the wave's end load out of range (zeros) and write nothing.
-template <int D>
+// Workgroup b covers K split b % nsplit; with wps workgroups per split, wave
+// w of workgroup r is wave gw = r * kBWaves + w of the split and takes the
+// 16-row units gw, gw + GW, ... (GW = wps * kBWaves), so the chip sweeps the
+// matrix front to back.  A wave streams (unit, group) items through a ring of
+// D register slots: each slot is refilled with the item D places later as
+// soon as it is consumed, so D items of weights stay in flight with no
+// barrier in the loop.  The weights of an item (16 rows x 128 B) arrive as
+// whole 128-byte lines, 8 rows per load instruction, and are turned into the
+// MFMA B layout (lane (j, kg): row j, chunks kg and 4 + kg) through a small
+// per-wave LDS tile.  With kSmQuad (groups per split a multiple of 4) the
+// (scale, minimum) pairs come 4 groups per load, lane (j, kg) holding group
+// 4q + kg of row j, and reach the other lanes by a cross-lane read.  Items
+// past the wave's end load out of range (zeros) and write nothing.
+constexpr int kBTileRow = 9 * 16;                  // 8 chunks of 16 B + 16 B pad
+constexpr int kBTileLds = kBRows * kBTileRow;      // transposition tile per wave
+
+template <int D, bool kSmQuad>
 __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict__ x,
                                                          const uint8_t *__restrict__ qs,
                                                          const uint32_t *__restrict__ sm,
                                                          float *__restrict__ out, int64_t ldo, int M,
                                                          int N, int K, int gps, int nsplit, int wps)
 {
+    static_assert(!kSmQuad || D % 4 == 0, "quads of slots");
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     const int lane = threadIdx.x & 63, j = lane & 15, kg = lane >> 4;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x % nsplit, wr = blockIdx.x / nsplit;
     const int GK = K / kGroup;
     const int g0 = split * gps;
     const int gc = min(GK, g0 + gps) - g0;  // >= 1: the host makes every split non-empty
     const int R = (N + kBRows - 1) / kBRows;
-    const int rb0 = (int)((int64_t)R * wr / wps), rb1 = (int)((int64_t)R * (wr + 1) / wps);
-    const int nunits = rb1 - rb0 > wave ? (rb1 - rb0 - wave + kBWaves - 1) / kBWaves : 0;
+    const int gw = wr * kBWaves + wave, GW = wps * kBWaves;
+    const int nunits = R > gw ? (R - gw + GW - 1) / GW : 0;
     const int nitems = nunits * gc;
     const uint32_t rowbytes = K / 2;
     float *dst = out + (int64_t)split * M * ldo;  // partials: [split][M][ldo]
+    uint8_t *tile = xl + arm_b_x_lds_bytes(gc) + wave * kBTileLds;
 
     const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowbytes);
     const rsrc_t r_sm = make_rsrc(sm, (uint32_t)N * GK * 4u);
-    uint4 wq[D][2];   // bytes 32kg..32kg+31 of group g of weight row 16 unit + j
-    uint32_t wsm[D];  // (scale, minimum) of that row and group
+    uint4 wq[D][2];                     // rows 16 u + (lane >> 3) and + 8, chunk lane & 7
+    uint32_t wsm[kSmQuad ? D / 4 : D];  // (scale, minimum) pairs
     auto load_item = [&](int s, int unit, int gl) {
         const bool ok = unit < nunits;
-        const int n = min((rb0 + wave + kBWaves * unit) * kBRows + j, N);  // row N reads zeros
-        const uint32_t o = ok ? (uint32_t)n * rowbytes + (uint32_t)(g0 + gl) * 128u + kg * 32 : 0x80000000u;
-        const uint32_t os = ok ? ((uint32_t)n * GK + g0 + gl) * 4u : 0x80000000u;
-        wq[s][0] = buf_load16(r_qs, o);
-        wq[s][1] = buf_load16(r_qs, o + 16);
-        wsm[s] = buf_load4(r_sm, os);
+        const int r0 = (gw + GW * unit) * kBRows + (lane >> 3);
+        const uint32_t gb = (uint32_t)(g0 + gl) * 128u + (lane & 7) * 16;
+        // rows past N read zeros (row N is out of the descriptor's range)
+        const uint32_t o0 = ok ? (uint32_t)min(r0, N) * rowbytes + gb : 0x80000000u;
+        const uint32_t o1 = ok ? (uint32_t)min(r0 + 8, N) * rowbytes + gb : 0x80000000u;
+        wq[s][0] = buf_load16_nt(r_qs, o0);
+        wq[s][1] = buf_load16_nt(r_qs, o1);
+        if (!kSmQuad) {
+            const int n = min((gw + GW * unit) * kBRows + j, N);
+            wsm[s] = buf_load4_nt(r_sm, ok ? ((uint32_t)n * GK + g0 + gl) * 4u : 0x80000000u);
+        }
     };
+    // pairs of groups gl .. gl+3 of the unit: lane (j, kg) takes group gl + kg of row j
+    auto load_quad = [&](int q, int unit, int gl) {
+        const bool ok = unit < nunits;
+        const int n = min((gw + GW * unit) * kBRows + j, N);
+        wsm[q] = buf_load4_nt(r_sm, ok ? ((uint32_t)n * GK + g0 + gl + kg) * 4u : 0x80000000u);
+    };
+    // activation loads first, then the weight ring, then the conversion
+    const rsrc_t r_x = make_rsrc(x, (uint32_t)M * K * 4u);
+    const int nx = kBRows * gc * 32;
+    XGroupItems xv;
+    load_x_groups(r_x, M, K, g0, gc, 0, xv);
     int lu = 0, lg = 0;  // next item to load
 #pragma unroll
     for (int s = 0; s < D; ++s) {
         load_item(s, lu, lg);
+        if (kSmQuad && s % 4 == 3) load_quad(s / 4, lu, lg - 3);
         if (++lg == gc) { lg = 0; ++lu; }
     }
-    fill_x_groups(x, M, K, g0, gc, xl);
+    convert_x_groups(gc, 0, xv, xl);
+    for (int base = kXBatch * kBThreads; base < nx; base += kXBatch * kBThreads) {
+        load_x_groups(r_x, M, K, g0, gc, base, xv);
+        convert_x_groups(gc, base, xv, xl);
+    }
     __syncthreads();
 
     const float *fac = reinterpret_cast<const float *>(xl + (size_t)gc * kBGroupLds);
@@ -510,31 +568,46 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             // the previous item's epilogue completes before this item's LDS
-            // reads are issued (only one item's operands are live at a time)
+            // traffic is issued (only one item's operands are live at a time)
             asm volatile("" : "+v"(yacc)::"memory");
+            // weights of slot s through the tile: row r at r * kBTileRow, chunk c at 16 c
+            *reinterpret_cast<uint4 *>(tile + (lane >> 3) * kBTileRow + (lane & 7) * 16) = wq[s][0];
+            *reinterpret_cast<uint4 *>(tile + (8 + (lane >> 3)) * kBTileRow + (lane & 7) * 16) = wq[s][1];
+            const uint4 bw0 = *reinterpret_cast<const uint4 *>(tile + j * kBTileRow + kg * 16);
+            const uint4 bw1 = *reinterpret_cast<const uint4 *>(tile + j * kBTileRow + (4 + kg) * 16);
+            const uint32_t smv = kSmQuad ? (uint32_t)__shfl((int)wsm[s / 4], j + 16 * (s % 4)) : wsm[s];
+            // slot s is consumed: refill it in place with the item D later
+            // (its (scale, minimum) quad once the last item using it is read)
+            asm volatile("" : "+v"(yacc)::"memory");
+            load_item(s, lu, lg);
+            if (kSmQuad && s % 4 == 3) load_quad(s / 4, lu, lg - 3);
+            if (++lg == gc) { lg = 0; ++lu; }
+
             const uint8_t *ag = xl + (size_t)cg * kBGroupLds + (kg * kBRows + j) * 16;
-            float4_t acc = {0.f, 0.f, 0.f, 0.f};
+            // two independent accumulator chains (even / odd steps)
+            float4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
                 const half8_t a = *reinterpret_cast<const half8_t *>(ag + d * 4 * kBRows * 16);
-                const uint4 c4 = wq[s][d >> 2];
+                const uint4 c4 = d < 4 ? bw0 : bw1;
                 const uint32_t w = (d & 3) == 0 ? c4.x : (d & 3) == 1 ? c4.y : (d & 3) == 2 ? c4.z : c4.w;
                 uint32_t p[4];
                 widen(w, p);
                 const half8_t b = __builtin_bit_cast(half8_t, uint4{p[0], p[1], p[2], p[3]});
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+                acc2[d & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc2[d & 1], 0, 0, 0);
             }
+            const float4_t acc = acc2[0] + acc2[1];
             const float4 f = *reinterpret_cast<const float4 *>(fac + (cg * 3 + 0) * kBRows + 4 * kg);
             const float4 X = *reinterpret_cast<const float4 *>(fac + (cg * 3 + 1) * kBRows + 4 * kg);
             const float4 cc = *reinterpret_cast<const float4 *>(fac + (cg * 3 + 2) * kBRows + 4 * kg);
-            const float sf = f16_bits_to_f32(wsm[s] & 0xFFFFu), mf = f16_bits_to_f32(wsm[s] >> 16);
+            const float sf = f16_bits_to_f32(smv & 0xFFFFu), mf = f16_bits_to_f32(smv >> 16);
             yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
             yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
             yacc[2] = fmaf(sf, fmaf(f.z, acc[2], cc.z), fmaf(mf, X.z, yacc[2]));
             yacc[3] = fmaf(sf, fmaf(f.w, acc[3], cc.w), fmaf(mf, X.w, yacc[3]));
             if (cg == gc - 1) {
                 // unit complete: lane (j, kg) holds rows m = 4kg+e of column n
-                const int n = (rb0 + wave + kBWaves * cu) * kBRows + j;
+                const int n = (gw + GW * cu) * kBRows + j;
                 if (cu < nunits && n < N) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -546,10 +619,6 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
             } else {
                 ++cg;
             }
-            // slot s is consumed: refill it in place with the item D later
-            asm volatile("" : "+v"(yacc)::"memory");
-            load_item(s, lu, lg);
-            if (++lg == gc) { lg = 0; ++lu; }
         }
     }
 }
@@ -636,9 +705,16 @@ static hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, con
     // split-K partials are dense [nsplit][M][N]; otherwise y is written directly
     float *out = c.nsplit > 1 ? static_cast<float *>(workspace) : y;
     const int64_t ldo = c.nsplit > 1 ? N : ldy;
-    hipLaunchKernelGGL((k_gemv_mfma<kBDepth>), dim3((unsigned)(wps * c.nsplit)), dim3(kBThreads), lds,
-                       stream, x, qs, reinterpret_cast<const uint32_t *>(sm), out, ldo, M, (int)N, K,
-                       c.gps, c.nsplit, (int)wps);
+    // (scale, minimum) quads need every split's group count to be a multiple of 4
+    const bool quad = (K / kGroup) % c.gps == 0 && c.gps % 4 == 0;
+    if (quad)
+        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, true>), dim3((unsigned)(wps * c.nsplit)), dim3(kBThreads),
+                           lds, stream, x, qs, reinterpret_cast<const uint32_t *>(sm), out, ldo, M, (int)N,
+                           K, c.gps, c.nsplit, (int)wps);
+    else
+        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, false>), dim3((unsigned)(wps * c.nsplit)), dim3(kBThreads),
+                           lds, stream, x, qs, reinterpret_cast<const uint32_t *>(sm), out, ldo, M, (int)N,
+                           K, c.gps, c.nsplit, (int)wps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.nsplit == 1) return e;
     const int64_t count = (int64_t)M * N;
