@@ -21,7 +21,10 @@ Algorithmic bytes of a GEMV: packed weights N*K/2 + scales N*K/256*4 + x M*K*4
 + y M*N*4.  Packing (q4_pack) is setup and is not timed.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --pmc-workload   (lm_head GEMV and a 256 MiB copy, 3 launches
+                                         each, for hardware-counter runs; prints nothing)
 """
+import hashlib
 import argparse
 import json
 import os
@@ -56,7 +59,63 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the decode layers one by one")
     ap.add_argument("--no-tiny-m", action="store_true", help="skip the tiny-M GEMV sweep")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="only launch the lm_head GEMV and a 256 MiB copy (for rocprofv3 --pmc)")
     return ap.parse_args()
+
+
+# HBM bytes of the lm_head GEMV launch from rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE runs over --pmc-workload, scaled by the same counters on the copy).
+# They describe the kernel source they were taken on; a changed source has not
+# been measured, so the figure is then withheld.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "lm_head_gemv_hbm_counters.md")
+GEMV_SOURCES = [os.path.join(ROOT, "bit_quantized_matmul_q4_amd", "csrc", f)
+                for f in ("gemv.hip", "q4mi_device.h")]
+
+
+def gemv_source_hash():
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("traffic-record "):
+            for kv in line.split()[1:]:
+                k, _, v = kv.partition("=")
+                fields[k] = v
+    if fields.get("gemv_sha256") != gemv_source_hash() or "bytes_per_launch" not in fields:
+        return None
+    return int(fields["bytes_per_launch"])
+
+
+def pmc_workload():
+    """lm_head GEMV x3 and a 256 MiB device copy x3, nothing timed or printed."""
+    import torch
+    import bit_quantized_matmul_q4_amd as q4
+    from bit_quantized_matmul_q4_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    _, K, N = wl.DECODE_PROJECTIONS[7]
+    g = wl.generator(7, dev)
+    W = wl.draw_weights(g, N, K, dev)
+    qs, sm = q4.q4_pack(W)
+    del W
+    x = wl.draw_activations(wl.generator(12345, dev), 1, K, False, dev)
+    y = torch.empty((1, N), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        q4.q4_gemv(x, qs, sm, y=y)
+    src = torch.ones((64 << 20,), dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(wl):
@@ -139,6 +198,63 @@ def tiny_m_sweep(q4, wl, dev, stream, reps=6):
     return res
 
 
+def graph_launch_us(fn, n, stream):
+    """Median per-launch time (us) of n launches captured by fn() into one graph."""
+    import torch
+    fn()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        times.append((a, b))
+    torch.cuda.synchronize()
+    return sorted(x.elapsed_time(y) for x, y in times)[2] * 1e3 / n
+
+
+def decode_breakdown(q4, layers, xs, stream):
+    """Each projection of the decode set on its own: its 36 per-layer launches
+    (distinct weights) replayed as one graph; per-launch time and GB/s."""
+    res = {}
+    for k in range(len(layers[0])):
+        name, K, N = layers[0][k][:3]
+        launches = [layers[layer][k] for layer in range(len(layers))]
+
+        def run():
+            for (_, K_, N_, qs, sm, y) in launches:
+                q4.q4_gemv(xs[K_], qs, sm, y=y)
+        us = graph_launch_us(run, len(launches), stream)
+        res[name] = {"K": K, "N": N, "us": round(us, 2),
+                     "gbs": round(gemv_bytes(1, N, K) / (us * 1e-6) / 1e9, 1)}
+    return res
+
+
+def single_gemv(q4, wl, dev, stream):
+    """The 4096 x 4096 GEMV (seed 0) alone: 60 copies of its packed weights
+    (521 MB, beyond the Infinity Cache) launched in turn from one graph."""
+    import torch
+    c = wl.SINGLE_GEMV
+    W, x = wl.gemv_case(c["seed"], 1, c["N"], c["K"], dev)
+    qs, sm = q4.q4_pack(W)
+    del W
+    copies = [(qs.clone(), sm.clone()) for _ in range(60)]
+    y = torch.empty((1, c["N"]), dtype=torch.float32, device=dev)
+
+    def run():
+        for (q, s_) in copies:
+            q4.q4_gemv(x, q, s_, y=y)
+    us = graph_launch_us(run, len(copies), stream)
+    nbytes = gemv_bytes(1, c["N"], c["K"])
+    return {"N": c["N"], "K": c["K"], "us": round(us, 2),
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -146,6 +262,9 @@ def main():
               "(the multi-GPU sharding is a design note, not an implementation)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.pmc_workload:
+        pmc_workload()
+        return
 
     import torch
     import bit_quantized_matmul_q4_amd as q4
@@ -285,7 +404,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4 x f16(hi+lo) -> f32 (GEMV); i8 x u4 -> i32 (MMQ)",
+        "dtype": "u4 x f16 -> f32 (GEMV); i8 x u4 -> i32 (MMQ)",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; random weights of the stated shapes)",
         "config": {
             "workload": "decode token of a ~4B dense transformer at M=1: 36 layers x "
@@ -309,13 +428,15 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "mmq_prefill": dict(mmq_rep, roofline={
             "kernel": "k_mmq (M=2048, K=4096, N=12288)", "bound": "mfma",
             "achieved": big["tops"], "peak": I8_PEAK_TOPS, "unit": "TOP/s",
             "frac": round(big["tops"] / I8_PEAK_TOPS, 4)}),
     }
+    out["decode_projections"] = decode_breakdown(q4, layers, xs, stream)
+    out["gemv_single_4096"] = single_gemv(q4, wl, dev, stream)
     if not args.no_tiny_m:
         out["gemv_tiny_m"] = tiny_m_sweep(q4, wl, dev, stream)
     if not args.no_cpu_baseline:
