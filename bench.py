@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the decode layers one by one")
     ap.add_argument("--no-tiny-m", action="store_true", help="skip the tiny-M GEMV sweep")
+    ap.add_argument("--no-prefill-sweep", action="store_true",
+                    help="skip the pp = 256..2048 MMQ sweep and the GEMV/MMQ crossover")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="only launch the lm_head GEMV and a 256 MiB copy (for rocprofv3 --pmc)")
     return ap.parse_args()
@@ -255,6 +257,84 @@ def single_gemv(q4, wl, dev, stream):
             "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def launch_floor_us(stream, n=252):
+    """Per-launch time of a one-element fill kernel replayed n times in a graph:
+    the dispatch floor every decode launch pays on this system."""
+    import torch
+    t = [torch.zeros(1, device="cuda") for _ in range(n)]
+
+    def run():
+        for v in t:
+            v.fill_(1.0)
+    return round(graph_launch_us(run, n, stream), 3)
+
+
+def prefill_sweep(q4, wl, dev, stream):
+    """MMQ (with and without its Q8_1 pass) at pp = 256..2048 on the ~9B-shaped
+    layer pair, and the GEMV/MMQ crossover at M = 16..256 on the 4096 -> 12288
+    layer: the GEMV path runs ceil(M/16) launches of 16 rows, the MMQ path
+    Q8_1 + MMQ.  Median of 5 event-timed repetitions each."""
+    import torch
+
+    def timed(fn, reps=5):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return sorted(x.elapsed_time(y) for x, y in ts)[len(ts) // 2] * 1e3
+
+    out = {"pp": {}, "crossover": {}}
+    layers = []
+    for c in wl.MMQ_2048:
+        g = wl.generator(c["seed"], dev)
+        W = wl.draw_weights(g, c["N"], c["K"], dev)
+        qs, sm = q4.q4_pack(W)
+        del W
+        layers.append((c, qs, sm))
+    for pp in (256, 512, 1024, 2048):
+        row = {}
+        for (c, qs, sm) in layers:
+            K, N = c["K"], c["N"]
+            x = wl.draw_activations(wl.generator(c["seed"], dev), pp, K, True, dev)
+            qa = torch.empty((pp, K), dtype=torch.int8, device=dev)
+            ds = torch.empty((pp, K // 32, 2), dtype=torch.float16, device=dev)
+            y = torch.empty((pp, N), dtype=torch.float32, device=dev)
+            q8_us = timed(lambda: q4.q8_1_quantize(x, qa, ds))
+            mmq_us = timed(lambda: q4.q4_mmq_gemm(qa, ds, qs, sm, y=y))
+            ops = 2.0 * pp * N * K
+            row[c["name"]] = {"mmq_us": round(mmq_us, 1), "q8_1_us": round(q8_us, 1),
+                              "tops": round(ops / (mmq_us * 1e-6) / 1e12, 1),
+                              "tops_incl_q8_1": round(ops / ((mmq_us + q8_us) * 1e-6) / 1e12, 1)}
+        tot = sum(v["mmq_us"] + v["q8_1_us"] for v in row.values())
+        row["tokens_per_s_layer_pair"] = round(pp / (tot * 1e-6), 1)
+        out["pp"][str(pp)] = row
+    c, qs, sm = layers[0]
+    K, N = c["K"], c["N"]
+    for M in (16, 32, 64, 128, 256):
+        x = wl.draw_activations(wl.generator(M, dev), M, K, False, dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = torch.empty((max(1, q4.q4_gemv_workspace_bytes(16, N, K)),), dtype=torch.uint8, device=dev)
+
+        def gemv_path():
+            for r in range(0, M, 16):
+                q4.q4_gemv(x[r:r + 16], qs, sm, y=y[r:r + 16], workspace=ws)
+        qa = torch.empty((M, K), dtype=torch.int8, device=dev)
+        ds = torch.empty((M, K // 32, 2), dtype=torch.float16, device=dev)
+
+        def mmq_path():
+            q4.q8_1_quantize(x, qa, ds)
+            q4.q4_mmq_gemm(qa, ds, qs, sm, y=y)
+        g_us, m_us = timed(gemv_path), timed(mmq_path)
+        out["crossover"]["M%d" % M] = {"gemv_us": round(g_us, 1), "mmq_us": round(m_us, 1),
+                                       "faster": "gemv" if g_us < m_us else "mmq"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -436,9 +516,12 @@ def main():
             "frac": round(big["tops"] / I8_PEAK_TOPS, 4)}),
     }
     out["decode_projections"] = decode_breakdown(q4, layers, xs, stream)
+    out["graph_launch_floor_us"] = launch_floor_us(stream)
     out["gemv_single_4096"] = single_gemv(q4, wl, dev, stream)
     if not args.no_tiny_m:
         out["gemv_tiny_m"] = tiny_m_sweep(q4, wl, dev, stream)
+    if not args.no_prefill_sweep:
+        out["prefill_sweep"] = prefill_sweep(q4, wl, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(512, kDots ? 1 : 4) void k_mmq(const int8_t *__rest
                                                             float *__restrict__ y,
                                                             int32_t *__restrict__ idot, int M, int N,
                                                             int K, int tiles_m, int64_t ldy,
-                                                            int64_t ldi, int vec_store)
+                                                            int64_t ldi, int vec_store, int gps)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTotal];
     uint8_t *const sA = lds;
@@ -99,6 +99,10 @@ __global__ __launch_bounds__(512, kDots ? 1 : 4) void k_mmq(const int8_t *__rest
     const int mt = tile % tiles_m, nt = tile / tiles_m;
     const int n0 = nt * kTile, m0 = mt * kTile;
     const int G = K / kGroup, B = K / kBlock;
+    // K split blockIdx.y covers groups [g_lo, g_hi); its partial sums go to
+    // their own [M][ldy] slice of y (the caller's workspace when split)
+    const int g_lo = blockIdx.y * gps, g_hi = min(G, g_lo + gps);
+    if (!kDots) y += (int64_t)blockIdx.y * M * ldy;
     const uint32_t rowA = K / 2;
 
     const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowA);
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(512, kDots ? 1 : 4) void k_mmq(const int8_t *__rest
 
     const int arow_w = wm * 32 + l32;  // this lane's activation row in the tile
 #pragma unroll 1
-    for (int g = 0; g < G; ++g) {
+    for (int g = g_lo; g < g_hi; ++g) {
         stage_group(g);
 
         // ---- 8 blocks x 2 tiles: MFMA + per-block epilogue ----
@@ -273,15 +277,56 @@ __global__ __launch_bounds__(512, kDots ? 1 : 4) void k_mmq(const int8_t *__rest
     }
 }
 
+// y[m][n] (row stride ldy) = sum over splits of partial[s][m][n] (dense
+// [nsplit][M][N]), in split order
+__global__ __launch_bounds__(256) void k_mmq_split_sum(const float *__restrict__ partial,
+                                                       float *__restrict__ y, int M, int N,
+                                                       int64_t ldy, int nsplit)
+{
+    const int64_t count = (int64_t)M * N;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        float v = 0.0f;
+        for (int s = 0; s < nsplit; ++s) v += partial[(int64_t)s * count + i];
+        y[(i / N) * ldy + i % N] = v;
+    }
+}
+
+// K is split while the grid has at most one workgroup per CU of a full MI355X
+// (one resident workgroup cannot hide its own staging; beyond that the
+// partials' extra traffic costs more than the split gains).  The split
+// depends only on the shape, so the workspace size does too.
+constexpr int64_t kSplitCus = 256;
+
+struct SplitCfg {
+    int nsplit, gps;
+};
+
+SplitCfg choose_split(int64_t M, int64_t N, int K)
+{
+    const int G = K / kGroup;
+    const int64_t tiles = ((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
+    int s = 1;
+    // halve K ranges while the grid is at most one workgroup per CU and each keeps >= 2 groups
+    while (tiles * s <= kSplitCus && (G + 2 * s - 1) / (2 * s) >= 2) s *= 2;
+    SplitCfg c;
+    c.gps = (G + s - 1) / s;
+    c.nsplit = (G + c.gps - 1) / c.gps;  // every split non-empty
+    return c;
+}
+
 // Run over sub-problems whose weights (N rows) and activations (M rows) each
 // stay below 2 GiB, the reach of a buffer descriptor with 32-bit offsets.
+// With a K split, each sub-problem's partials go to the workspace (dense
+// [nsplit][mm][nn]) and are summed into y by a second kernel.
 hipError_t run_tiles(bool dots, const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
-                     const uint16_t *sm, int64_t N, int K, float *y, int32_t *idot,
-                     hipStream_t stream)
+                     const uint16_t *sm, int64_t N, int K, float *y, int32_t *idot, void *workspace,
+                     int num_cus, hipStream_t stream)
 {
     const int64_t n_max = ((kMaxBufferBytes - 1) / (K / 2)) / kTile * kTile;
     const int64_t m_max = ((kMaxBufferBytes - 1) / K) / kTile * kTile;
     const int B = K / kBlock;
+    const SplitCfg sc = dots ? SplitCfg{1, K / kGroup} : choose_split(M, N, K);
     for (int64_t m0 = 0; m0 < M; m0 += m_max) {
         const int64_t mm = M - m0 < m_max ? M - m0 : m_max;
         for (int64_t n0 = 0; n0 < N; n0 += n_max) {
@@ -295,16 +340,24 @@ hipError_t run_tiles(bool dots, const int8_t *qa, const uint16_t *ds, int64_t M,
                 hipLaunchKernelGGL(k_mmq<true>, dim3((unsigned)tiles), dim3(512), 0, stream, qa0,
                                    (const uint32_t *)nullptr, qs0, (const uint32_t *)nullptr,
                                    (float *)nullptr, idot + (m0 * N + n0) * B, (int)mm, (int)nn, K,
-                                   tiles_m, (int64_t)0, N * B, 0);
+                                   tiles_m, (int64_t)0, N * B, 0, sc.gps);
             } else {
                 float *y0 = y + m0 * N + n0;
-                const int vec_store = (N % 4 == 0) && (nn % 4 == 0) &&
-                                      ((reinterpret_cast<uintptr_t>(y0) & 15) == 0);
-                hipLaunchKernelGGL(k_mmq<false>, dim3((unsigned)tiles), dim3(512), 0, stream, qa0,
-                                   reinterpret_cast<const uint32_t *>(ds + m0 * B * 2), qs0,
-                                   reinterpret_cast<const uint32_t *>(sm + n0 * (K / kGroup) * 2), y0,
-                                   (int32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, N, (int64_t)0,
-                                   vec_store);
+                float *out = sc.nsplit > 1 ? static_cast<float *>(workspace) : y0;
+                const int64_t ldo = sc.nsplit > 1 ? nn : N;
+                const int vec_store = (ldo % 4 == 0) && (nn % 4 == 0) &&
+                                      ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+                hipLaunchKernelGGL(k_mmq<false>, dim3((unsigned)tiles, (unsigned)sc.nsplit), dim3(512), 0,
+                                   stream, qa0, reinterpret_cast<const uint32_t *>(ds + m0 * B * 2), qs0,
+                                   reinterpret_cast<const uint32_t *>(sm + n0 * (K / kGroup) * 2), out,
+                                   (int32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, ldo, (int64_t)0,
+                                   vec_store, sc.gps);
+                if (sc.nsplit > 1 && hipGetLastError() == hipSuccess) {
+                    int64_t sb = (mm * nn + 255) / 256;
+                    if (sb > (int64_t)num_cus * 8) sb = (int64_t)num_cus * 8;
+                    hipLaunchKernelGGL(k_mmq_split_sum, dim3((unsigned)sb), dim3(256), 0, stream, out, y0,
+                                       (int)mm, (int)nn, N, sc.nsplit);
+                }
             }
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
@@ -315,19 +368,29 @@ hipError_t run_tiles(bool dots, const int8_t *qa, const uint16_t *ds, int64_t M,
 
 }  // namespace
 
-size_t mmq_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 1 || N < 1 || K < kGroup) return 0;
+    const SplitCfg sc = choose_split(M, N, (int)K);
+    if (sc.nsplit == 1) return 0;
+    // the largest sub-problem's partials (sub-problems split at < 2 GiB reach)
+    const int64_t n_max = ((kMaxBufferBytes - 1) / (K / 2)) / kTile * kTile;
+    const int64_t m_max = ((kMaxBufferBytes - 1) / K) / kTile * kTile;
+    const int64_t mm = M < m_max ? M : m_max, nn = N < n_max ? N : n_max;
+    return (size_t)sc.nsplit * mm * nn * sizeof(float);
+}
 
 hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
-                      const uint16_t *sm, int64_t N, int K, float *y, void *, const DeviceInfo &,
-                      hipStream_t stream)
+                      const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
+                      const DeviceInfo &dev, hipStream_t stream)
 {
-    return run_tiles(false, qa, ds, M, qs, sm, N, K, y, nullptr, stream);
+    return run_tiles(false, qa, ds, M, qs, sm, N, K, y, nullptr, workspace, dev.num_cus, stream);
 }
 
 hipError_t launch_block_dots(const int8_t *qa, int64_t M, const uint8_t *qs, int64_t N, int K,
-                             int32_t *idot, const DeviceInfo &, hipStream_t stream)
+                             int32_t *idot, const DeviceInfo &dev, hipStream_t stream)
 {
-    return run_tiles(true, qa, nullptr, M, qs, nullptr, N, K, nullptr, idot, stream);
+    return run_tiles(true, qa, nullptr, M, qs, nullptr, N, K, nullptr, idot, nullptr, dev.num_cus, stream);
 }
 
 }  // namespace q4mi

@@ -307,6 +307,23 @@ def test_mmq_2048_full(q4, orc, idx):
     mmq_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq 2048 " + c["name"], mrows=rows)
 
 
+def test_mmq_split_k_small(q4, orc):
+    # 2 output tiles and 8 groups of K: the launch splits K four ways and sums
+    # the partials in a second pass
+    say("mmq K split: M=100 N=200 K=2048 (4 splits)")
+    assert q4.q4_mmq_workspace_bytes(100, 200, 2048) == 4 * 100 * 200 * 4
+    mmq_check(q4, orc, 100, 200, 2048, 41, True, "mmq split 100x200x2048")
+
+
+def test_mmq_split_k_pp256_down(q4, orc):
+    # the 12288 -> 4096 prefill layer at 256 tokens: 64 tiles, K split 8 ways
+    c = wl.MMQ_2048[1]
+    say("mmq K split: M=256 K=%d N=%d (sampled activation rows)" % (c["K"], c["N"]))
+    assert q4.q4_mmq_workspace_bytes(256, c["N"], c["K"]) == 8 * 256 * c["N"] * 4
+    rows = np.unique(np.concatenate([[0, 255], np.random.default_rng(7).choice(256, 30, replace=False)]))
+    mmq_check(q4, orc, 256, c["N"], c["K"], c["seed"], True, "mmq pp256 down", mrows=rows)
+
+
 def test_mmq_m1_matches_gemv_on_dequantized_row(q4, orc):
     say("mmq M=1 vs gemv on the dequantized Q8_1 row")
     W, x = wl.mmq_case(5, 1, 777, 2560)
