@@ -7,9 +7,10 @@ resident in HBM:
   decode leg  -- one decoded token of a ~4B dense transformer at M = 1: the
                  projection set q, k, v (2560 -> 4096/1024/1024), o
                  (4096 -> 2560), gate, up (2560 -> 9216), down (9216 -> 2560)
-                 for each of 36 layers with distinct weights, replayed as one
-                 HIP graph, then the lm_head GEMV (2560 -> 151936) launched
-                 on its own between HIP events.  2.01 GB of packed weights per
+                 for each of 36 layers with distinct weights (q/k/v and gate/up
+                 as row-concatenated matrices, 4 launches per layer), replayed
+                 as one HIP graph, then the lm_head GEMV (2560 -> 151936)
+                 launched on its own between HIP events.  2.01 GB of packed weights per
                  token, far above the 256 MB Infinity Cache.
   prefill leg -- Q8_1 quantization of the activations followed by the MMQ
                  GEMM for M = 2048 tokens on a ~9B-shaped layer pair
@@ -372,10 +373,26 @@ def main():
             y = torch.empty((1, N), dtype=torch.float32, device=dev)
             projs.append((name, K, N, qs, sm, y))
         layers.append(projs)
+    # The timed step runs each layer in the usual fused layouts: q, k, v as one
+    # row-concatenated 2560 -> 6144 matrix and gate, up as one 2560 -> 18432
+    # matrix (packing is per row, so the concatenated packed tensors are the
+    # packed concatenation), i.e. 4 launches per layer: qkv, o, gate_up, down.
+    # The 7-launch stream over the separate matrices is reported beside it.
+    fused_layers = []
+    for projs in layers:
+        by = {p[0]: p for p in projs}
+
+        def cat(names):
+            qs = torch.cat([by[n][3] for n in names], 0)
+            sm = torch.cat([by[n][4] for n in names], 0)
+            return ("_".join(names), by[names[0]][1], qs.shape[0], qs, sm,
+                    torch.empty((1, qs.shape[0]), dtype=torch.float32, device=dev))
+        fused_layers.append([cat(["q", "k", "v"]), by["o"], cat(["gate", "up"]), by["down"]])
     _, Kl, Nl = wl.DECODE_PROJECTIONS[7]
     lm_qs, lm_sm = packed(7, Nl, Kl)
     lm_y = torch.empty((1, Nl), dtype=torch.float32, device=dev)
-    layer_bytes = sum(gemv_bytes(1, N, K) for (_, K, N) in wl.DECODE_PROJECTIONS[:7])
+    layer_bytes = sum(gemv_bytes(1, N, K) for (_, K, N, *_r) in fused_layers[0])
+    unfused_layer_bytes = sum(gemv_bytes(1, N, K) for (_, K, N) in wl.DECODE_PROJECTIONS[:7])
     lm_bytes = gemv_bytes(1, Nl, Kl)
     decode_bytes = LAYERS * layer_bytes + lm_bytes
 
@@ -396,6 +413,11 @@ def main():
     torch.cuda.synchronize()
 
     def decode_layers():
+        for projs in fused_layers:
+            for (name, K, N, qs, sm, y) in projs:
+                q4.q4_gemv(xs[K], qs, sm, y=y)
+
+    def decode_layers_unfused():
         for projs in layers:
             for (name, K, N, qs, sm, y) in projs:
                 q4.q4_gemv(xs[K], qs, sm, y=y)
@@ -489,7 +511,8 @@ def main():
         "config": {
             "workload": "decode token of a ~4B dense transformer at M=1: 36 layers x "
                         "{q,k,v 2560->4096/1024/1024, o 4096->2560, gate,up 2560->9216, down 9216->2560} "
-                        "+ lm_head 2560->151936, 4-bit group-256; plus MMQ prefill M=2048 "
+                        "+ lm_head 2560->151936, 4-bit group-256, q/k/v and gate/up as row-concatenated "
+                        "fused matrices (4 launches per layer); plus MMQ prefill M=2048 "
                         "(4096->12288, 12288->4096) and M=512 (2560->9216)",
             "decode_bytes_per_step": decode_bytes,
             "graph": graph is not None,
@@ -515,7 +538,17 @@ def main():
             "achieved": big["tops"], "peak": I8_PEAK_TOPS, "unit": "TOP/s",
             "frac": round(big["tops"] / I8_PEAK_TOPS, 4)}),
     }
+    n_unfused = LAYERS * len(layers[0])
+    unf_us = graph_launch_us(decode_layers_unfused, n_unfused, stream) * n_unfused
+    out["decode_unfused"] = {
+        "launches_per_layer": len(layers[0]),
+        "layers_us": round(unf_us, 1),
+        "layers_gbs": round(LAYERS * unfused_layer_bytes / (unf_us * 1e-6) / 1e9, 1),
+        "gbs_with_lm_head": round((LAYERS * unfused_layer_bytes + lm_bytes) /
+                                  ((unf_us + lm_ms * 1e3) * 1e-6) / 1e9, 1),
+    }
     out["decode_projections"] = decode_breakdown(q4, layers, xs, stream)
+    out["decode_projections_fused"] = decode_breakdown(q4, fused_layers, xs, stream)
     out["graph_launch_floor_us"] = launch_floor_us(stream)
     out["gemv_single_4096"] = single_gemv(q4, wl, dev, stream)
     if not args.no_tiny_m:
