@@ -659,9 +659,14 @@ MfmaCfg choose_mfma(int64_t N, int K)
 
 }  // namespace
 
+// Largest K whose activation image arm A holds in LDS (80 B per 32 of K plus
+// at most 2 KB of slice partials, within a workgroup's 160 KB); M = 1 calls
+// with a longer K take the matrix-core arm, which splits K over workgroups.
+constexpr int kArmAMaxK = 64512;
+
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    if (M <= 1) return 0;
+    if (M <= 1 && K <= kArmAMaxK) return 0;
     const MfmaCfg c = choose_mfma(N, (int)K);
     return c.nsplit > 1 ? (size_t)c.nsplit * M * N * sizeof(float) : 0;
 }
@@ -689,7 +694,7 @@ static hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, con
                                    int64_t N, int64_t ldy, int K, float *y, void *workspace,
                                    const DeviceInfo &dev, hipStream_t stream)
 {
-    if (M == 1) {
+    if (M == 1 && K <= kArmAMaxK) {
         const Dot2Cfg c = choose_dot2(N, K, dev);
         return c.G == 16 ? dispatch_dot2<16>(c, x, qs, sm, N, K, y, dev, stream)
                          : dispatch_dot2<8>(c, x, qs, sm, N, K, y, dev, stream);

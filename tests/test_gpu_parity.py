@@ -324,6 +324,25 @@ def test_mmq_split_k_pp256_down(q4, orc):
     mmq_check(q4, orc, 256, c["N"], c["K"], c["seed"], True, "mmq pp256 down", mrows=rows)
 
 
+def test_gemv_k_beyond_one_workgroup(q4, orc):
+    # K = 65792: the M = 1 activation image no longer fits one workgroup's
+    # LDS, so M = 1 runs on the matrix-core arm with K split over workgroups
+    K = 65792
+    assert q4.q4_gemv_workspace_bytes(1, 100, K) > 0
+    for M in (1, 3):
+        say("gemv M=%d N=100 K=%d" % (M, K))
+        W, x = wl.gemv_case(50 + M, M, 100, K)
+        qs, sm = q4.q4_pack(dev(W))
+        y = q4.q4_gemv(dev(x), qs, sm).cpu().numpy()
+        ref = orc.q4_gemv(x.numpy(), qs.cpu().numpy(), sm.cpu().view(torch.int16).numpy().view(np.uint16), K)
+        close(y, ref, "gemv K=%d M=%d" % (K, M))
+
+
+def test_mmq_long_k(q4, orc):
+    say("mmq M=130 N=100 K=65792")
+    mmq_check(q4, orc, 130, 100, 65792, 77, True, "mmq long K")
+
+
 def test_mmq_m1_matches_gemv_on_dequantized_row(q4, orc):
     say("mmq M=1 vs gemv on the dequantized Q8_1 row")
     W, x = wl.mmq_case(5, 1, 777, 2560)
