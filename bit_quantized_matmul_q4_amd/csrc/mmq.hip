@@ -48,7 +48,7 @@ constexpr int kLdsA = kTile * kRow;
 constexpr int kLdsB = kTile * kRow;
 constexpr int kLdsD = kTile * kBlocks * 4;   // d as fp32
 constexpr int kLdsX = kTile * 4;             // X[m][g] as fp32
-constexpr int kLdsSM = kTile * 8;            // (scale, minimum) as fp32
+constexpr int kLdsSM = kTile * 8;            // (scale, minimum) as fp32 pairs
 constexpr int kLdsStage = kLdsA + kLdsB + kLdsD + kLdsX + kLdsSM;
 constexpr int kLdsTotal = kLdsStage;
 
@@ -243,13 +243,17 @@ __global__ __launch_bounds__(512, kDots ? 1 : 4) void k_mmq(const int8_t *__rest
 
         if (!kDots) {
             // ---- group epilogue: weight scale and minimum ----
+            // rows 8q + 4 half + r (r = 0..3) of each tile are consecutive:
+            // two (scale, minimum) pairs per 16-byte read
             const float xm = sX[arow_w];
 #pragma unroll
             for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float2 smv = sSM[wn * 64 + ta * 32 + 8 * (e >> 2) + 4 * half + (e & 3)];
-                    yacc[ta][e] = fmaf(smv.x, gacc[ta][e], fmaf(smv.y, xm, yacc[ta][e]));
+                for (int p2 = 0; p2 < 8; ++p2) {
+                    const int e = 2 * p2;
+                    const float4 v = *reinterpret_cast<const float4 *>(sSM + wn * 64 + ta * 32 + 8 * (e >> 2) + 4 * half + (e & 3));
+                    yacc[ta][e] = fmaf(v.x, gacc[ta][e], fmaf(v.y, xm, yacc[ta][e]));
+                    yacc[ta][e + 1] = fmaf(v.z, gacc[ta][e + 1], fmaf(v.w, xm, yacc[ta][e + 1]));
                 }
         }
     }
