@@ -311,6 +311,13 @@ def prefill_sweep(q4, wl, dev, stream):
             row[c["name"]] = {"mmq_us": round(mmq_us, 1), "q8_1_us": round(q8_us, 1),
                               "tops": round(ops / (mmq_us * 1e-6) / 1e12, 1),
                               "tops_incl_q8_1": round(ops / ((mmq_us + q8_us) * 1e-6) / 1e12, 1)}
+            # handing the result on as Q8_1 (the next layer's input): quantizing
+            # in the GEMM epilogue vs the GEMM then a separate Q8_1 pass over y
+            qo = torch.empty((pp, N), dtype=torch.int8, device=dev)
+            dso = torch.empty((pp, N // 32, 2), dtype=torch.float16, device=dev)
+            fused_us = timed(lambda: q4.q4_mmq_gemm_q8_1(qa, ds, qs, sm, qa_out=qo, ds_out=dso))
+            sep_us = timed(lambda: (q4.q4_mmq_gemm(qa, ds, qs, sm, y=y), q4.q8_1_quantize(y, qo, dso)))
+            row[c["name"]]["q8_1_out"] = {"fused_us": round(fused_us, 1), "separate_us": round(sep_us, 1)}
         tot = sum(v["mmq_us"] + v["q8_1_us"] for v in row.values())
         row["tokens_per_s_layer_pair"] = round(pp / (tot * 1e-6), 1)
         out["pp"][str(pp)] = row

@@ -26,7 +26,7 @@ ERRORS = {
 GEMV_MAX_M = 16
 SYMBOLS = [
     "q4_abi_version", "q4_strerror", "q4_pack", "q8_1_quantize", "q4_gemv_workspace_bytes",
-    "q4_gemv", "q4_mmq_workspace_bytes", "q4_mmq_gemm", "q4_mmq_block_dots",
+    "q4_gemv", "q4_mmq_workspace_bytes", "q4_mmq_gemm", "q4_mmq_gemm_q8_1", "q4_mmq_block_dots",
 ]
 
 _lib = None
@@ -57,6 +57,7 @@ def lib():
         "q4_gemv": ([P, I64, P, P, I64, I64, P, P, SZ, P], I),
         "q4_mmq_workspace_bytes": ([I64, I64, I64], SZ),
         "q4_mmq_gemm": ([P, P, I64, P, P, I64, I64, P, P, SZ, P], I),
+        "q4_mmq_gemm_q8_1": ([P, P, I64, P, P, I64, I64, P, P, P, SZ, P], I),
         "q4_mmq_block_dots": ([P, I64, P, I64, I64, P, P], I),
     }
     for name, (args, res) in sig.items():
@@ -178,6 +179,26 @@ def q4_mmq_gemm(qa, ds, qs, sm, y=None, workspace=None, stream=None):
     _check(lib().q4_mmq_gemm(_ptr(qa), _ptr(ds), M, _ptr(qs), _ptr(sm), N, K, _ptr(y), _ptr(ws),
                              wsb, _stream(stream, qa)), "q4_mmq_gemm")
     return y
+
+
+def q4_mmq_gemm_q8_1(qa, ds, qs, sm, qa_out=None, ds_out=None, workspace=None, stream=None):
+    """(qa_out int8 [M][N], ds_out float16 [M][N/32][2]) = Q8_1 of the MMQ result."""
+    M, K = qa.shape
+    N = qs.shape[0]
+    _need(qa, torch.int8, (M, K), "qa")
+    _need(ds, torch.float16, (M, K // 32, 2), "ds")
+    _need(qs, torch.uint8, (N, K // 2), "qs")
+    _need(sm, torch.float16, (N, K // 256, 2), "sm")
+    if qa_out is None:
+        qa_out = torch.empty((M, N), dtype=torch.int8, device=qa.device)
+    if ds_out is None:
+        ds_out = torch.empty((M, N // 32, 2), dtype=torch.float16, device=qa.device)
+    _need(qa_out, torch.int8, (M, N), "qa_out")
+    _need(ds_out, torch.float16, (M, N // 32, 2), "ds_out")
+    ws, wsb = _workspace(q4_mmq_workspace_bytes(M, N, K), workspace, qa.device)
+    _check(lib().q4_mmq_gemm_q8_1(_ptr(qa), _ptr(ds), M, _ptr(qs), _ptr(sm), N, K, _ptr(qa_out),
+                                  _ptr(ds_out), _ptr(ws), wsb, _stream(stream, qa)), "q4_mmq_gemm_q8_1")
+    return qa_out, ds_out
 
 
 def q4_mmq_block_dots(qa, qs, idot=None, stream=None):

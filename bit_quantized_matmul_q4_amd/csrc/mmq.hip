@@ -74,16 +74,19 @@ __device__ __forceinline__ int xcd_tile(int pid, int ntiles)
 // One LDS stage of ~75 KB and at most 128 VGPRs per lane, so two workgroups
 // share a CU (4 waves per SIMD) and one's staging and barriers overlap the
 // other's MFMA loop.
-template <bool kDots>
-__global__ __launch_bounds__(512, kDots ? 1 : 4) void k_mmq(const int8_t *__restrict__ qa,
-                                                            const uint32_t *__restrict__ ds,
-                                                            const uint8_t *__restrict__ qs,
-                                                            const uint32_t *__restrict__ sm,
-                                                            float *__restrict__ y,
-                                                            int32_t *__restrict__ idot, int M, int N,
-                                                            int K, int tiles_m, int64_t ldy,
-                                                            int64_t ldi, int vec_store, int gps)
+// Output modes: fp32 y; the int32 block dots (test hook); or y quantized to
+// Q8_1 along n in the epilogue (qo int8 [M][ldy], dso [M][ldy/32]) for a
+// consumer that takes Q8_1 activations.
+enum { kOutY = 0, kOutDots = 1, kOutQ8 = 2 };
+
+template <int kMode>
+__global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
+    const int8_t *__restrict__ qa, const uint32_t *__restrict__ ds, const uint8_t *__restrict__ qs,
+    const uint32_t *__restrict__ sm, float *__restrict__ y, int32_t *__restrict__ idot,
+    int8_t *__restrict__ qo, uint32_t *__restrict__ dso, int M, int N, int K, int tiles_m, int64_t ldy,
+    int64_t ldi, int vec_store, int gps)
 {
+    constexpr bool kDots = kMode == kOutDots;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTotal];
     uint8_t *const sA = lds;
     uint8_t *const sB = lds + kLdsA;
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(512, kDots ? 1 : 4) void k_mmq(const int8_t *__rest
     // K split blockIdx.y covers groups [g_lo, g_hi); its partial sums go to
     // their own [M][ldy] slice of y (the caller's workspace when split)
     const int g_lo = blockIdx.y * gps, g_hi = min(G, g_lo + gps);
-    if (!kDots) y += (int64_t)blockIdx.y * M * ldy;
+    if (kMode == kOutY) y += (int64_t)blockIdx.y * M * ldy;
     const uint32_t rowA = K / 2;
 
     const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowA);
@@ -258,7 +261,42 @@ __global__ __launch_bounds__(512, kDots ? 1 : 4) void k_mmq(const int8_t *__rest
         }
     }
 
-    if (!kDots) {
+    if (kMode == kOutQ8) {
+        // Each 32-row MFMA tile is one Q8_1 block along n for this lane's row
+        // m: 16 values here and 16 in lane ^ 32.  N is a multiple of 32, so a
+        // block lies wholly inside or outside [0, N).
+        const int m = m0 + arow_w;
+#pragma unroll
+        for (int ta = 0; ta < 2; ++ta) {
+            const int nb = n0 + wn * 64 + ta * 32;  // first n of the block
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(yacc[ta][e]));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const uint16_t d16 = q8_1_scale(amax);
+            const float df = f16_bits_to_f32(d16);
+            int sum = 0;
+            uint32_t packed[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                packed[q] = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int a = q8_1_code(yacc[ta][4 * q + r], df);
+                    sum += a;
+                    packed[q] |= ((uint32_t)a & 0xFFu) << (8 * r);
+                }
+            }
+            sum += __shfl_xor(sum, 32);
+            if (m < M && nb < N) {
+                // rows n = nb + 8q + 4 half + r: four runs of four codes
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint32_t *>(qo + (int64_t)m * ldy + nb + 8 * q + 4 * half) = packed[q];
+                if (half == 0) dso[(int64_t)m * (ldy / kBlock) + nb / kBlock] = q8_1_ds(d16, df, sum);
+            }
+        }
+    } else if (!kDots) {
         const int m = m0 + arow_w;
         if (m < M) {
 #pragma unroll
@@ -296,6 +334,48 @@ __global__ __launch_bounds__(256) void k_mmq_split_sum(const float *__restrict__
     }
 }
 
+// As k_mmq_split_sum, then the sums quantized to Q8_1 along n: eight lanes per
+// block of 32 outputs, four per lane (N is a multiple of 32).
+__global__ __launch_bounds__(256) void k_mmq_split_sum_q8(const float *__restrict__ partial,
+                                                          int8_t *__restrict__ qo,
+                                                          uint32_t *__restrict__ dso, int M, int N,
+                                                          int64_t ldq, int nsplit)
+{
+    const int64_t count = (int64_t)M * N, nvec4 = count / 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    // stride and nvec4 are multiples of 8: the 8 lanes of a block iterate together
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec4; i += stride) {
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s = 0; s < nsplit; ++s) {
+            const float4 p = reinterpret_cast<const float4 *>(partial + (int64_t)s * count)[i];
+            v[0] += p.x;
+            v[1] += p.y;
+            v[2] += p.z;
+            v[3] += p.w;
+        }
+        float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        const uint16_t d16 = q8_1_scale(amax);
+        const float df = f16_bits_to_f32(d16);
+        uint32_t packed = 0;
+        int sum = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int a = q8_1_code(v[t], df);
+            sum += a;
+            packed |= ((uint32_t)a & 0xFFu) << (8 * t);
+        }
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        const int64_t m = (4 * i) / N, n = (4 * i) % N;
+        *reinterpret_cast<uint32_t *>(qo + m * ldq + n) = packed;
+        if ((i & 7) == 0) dso[m * (ldq / kBlock) + n / kBlock] = q8_1_ds(d16, df, sum);
+    }
+}
+
 // K is split while the grid has at most one workgroup per CU of a full MI355X
 // (one resident workgroup cannot hide its own staging; beyond that the
 // partials' extra traffic costs more than the split gains).  The split
@@ -322,15 +402,16 @@ SplitCfg choose_split(int64_t M, int64_t N, int K)
 // Run over sub-problems whose weights (N rows) and activations (M rows) each
 // stay below 2 GiB, the reach of a buffer descriptor with 32-bit offsets.
 // With a K split, each sub-problem's partials go to the workspace (dense
-// [nsplit][mm][nn]) and are summed into y by a second kernel.
-hipError_t run_tiles(bool dots, const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
-                     const uint16_t *sm, int64_t N, int K, float *y, int32_t *idot, void *workspace,
-                     int num_cus, hipStream_t stream)
+// [nsplit][mm][nn]) and a second kernel sums them into y (or into Q8_1).
+hipError_t run_tiles(int mode, const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                     const uint16_t *sm, int64_t N, int K, float *y, int32_t *idot, int8_t *qo,
+                     uint16_t *dso, void *workspace, int num_cus, hipStream_t stream)
 {
     const int64_t n_max = ((kMaxBufferBytes - 1) / (K / 2)) / kTile * kTile;
     const int64_t m_max = ((kMaxBufferBytes - 1) / K) / kTile * kTile;
     const int B = K / kBlock;
-    const SplitCfg sc = dots ? SplitCfg{1, K / kGroup} : choose_split(M, N, K);
+    const SplitCfg sc = mode == kOutDots ? SplitCfg{1, K / kGroup} : choose_split(M, N, K);
+    uint32_t *dso32 = reinterpret_cast<uint32_t *>(dso);
     for (int64_t m0 = 0; m0 < M; m0 += m_max) {
         const int64_t mm = M - m0 < m_max ? M - m0 : m_max;
         for (int64_t n0 = 0; n0 < N; n0 += n_max) {
@@ -340,28 +421,45 @@ hipError_t run_tiles(bool dots, const int8_t *qa, const uint16_t *ds, int64_t M,
             if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
             const int8_t *qa0 = qa + m0 * K;
             const uint8_t *qs0 = qs + n0 * (K / 2);
-            if (dots) {
-                hipLaunchKernelGGL(k_mmq<true>, dim3((unsigned)tiles), dim3(512), 0, stream, qa0,
+            const uint32_t *ds0 = reinterpret_cast<const uint32_t *>(ds + m0 * B * 2);
+            const uint32_t *sm0 = reinterpret_cast<const uint32_t *>(sm + n0 * (K / kGroup) * 2);
+            if (mode == kOutDots) {
+                hipLaunchKernelGGL(k_mmq<kOutDots>, dim3((unsigned)tiles), dim3(512), 0, stream, qa0,
                                    (const uint32_t *)nullptr, qs0, (const uint32_t *)nullptr,
-                                   (float *)nullptr, idot + (m0 * N + n0) * B, (int)mm, (int)nn, K,
-                                   tiles_m, (int64_t)0, N * B, 0, sc.gps);
-            } else {
-                float *y0 = y + m0 * N + n0;
-                float *out = sc.nsplit > 1 ? static_cast<float *>(workspace) : y0;
-                const int64_t ldo = sc.nsplit > 1 ? nn : N;
-                const int vec_store = (ldo % 4 == 0) && (nn % 4 == 0) &&
-                                      ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
-                hipLaunchKernelGGL(k_mmq<false>, dim3((unsigned)tiles, (unsigned)sc.nsplit), dim3(512), 0,
-                                   stream, qa0, reinterpret_cast<const uint32_t *>(ds + m0 * B * 2), qs0,
-                                   reinterpret_cast<const uint32_t *>(sm + n0 * (K / kGroup) * 2), out,
-                                   (int32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, ldo, (int64_t)0,
+                                   (float *)nullptr, idot + (m0 * N + n0) * B, (int8_t *)nullptr,
+                                   (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, (int64_t)0, N * B, 0,
+                                   sc.gps);
+            } else if (sc.nsplit > 1) {
+                // partials [nsplit][mm][nn] in the workspace, then the sum
+                float *part = static_cast<float *>(workspace);
+                const int vec_store = (nn % 4 == 0) ? 1 : 0;
+                hipLaunchKernelGGL(k_mmq<kOutY>, dim3((unsigned)tiles, (unsigned)sc.nsplit), dim3(512), 0,
+                                   stream, qa0, ds0, qs0, sm0, part, (int32_t *)nullptr, (int8_t *)nullptr,
+                                   (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, nn, (int64_t)0,
                                    vec_store, sc.gps);
-                if (sc.nsplit > 1 && hipGetLastError() == hipSuccess) {
+                if (hipGetLastError() == hipSuccess) {
                     int64_t sb = (mm * nn + 255) / 256;
                     if (sb > (int64_t)num_cus * 8) sb = (int64_t)num_cus * 8;
-                    hipLaunchKernelGGL(k_mmq_split_sum, dim3((unsigned)sb), dim3(256), 0, stream, out, y0,
-                                       (int)mm, (int)nn, N, sc.nsplit);
+                    if (mode == kOutY)
+                        hipLaunchKernelGGL(k_mmq_split_sum, dim3((unsigned)sb), dim3(256), 0, stream, part,
+                                           y + m0 * N + n0, (int)mm, (int)nn, N, sc.nsplit);
+                    else
+                        hipLaunchKernelGGL(k_mmq_split_sum_q8, dim3((unsigned)sb), dim3(256), 0, stream, part,
+                                           qo + m0 * N + n0, dso32 + m0 * (N / kBlock) + n0 / kBlock,
+                                           (int)mm, (int)nn, N, sc.nsplit);
                 }
+            } else if (mode == kOutY) {
+                float *y0 = y + m0 * N + n0;
+                const int vec_store = (N % 4 == 0) && (nn % 4 == 0) &&
+                                      ((reinterpret_cast<uintptr_t>(y0) & 15) == 0);
+                hipLaunchKernelGGL(k_mmq<kOutY>, dim3((unsigned)tiles, 1u), dim3(512), 0, stream, qa0, ds0, qs0,
+                                   sm0, y0, (int32_t *)nullptr, (int8_t *)nullptr, (uint32_t *)nullptr,
+                                   (int)mm, (int)nn, K, tiles_m, N, (int64_t)0, vec_store, sc.gps);
+            } else {
+                hipLaunchKernelGGL(k_mmq<kOutQ8>, dim3((unsigned)tiles, 1u), dim3(512), 0, stream, qa0, ds0,
+                                   qs0, sm0, (float *)nullptr, (int32_t *)nullptr, qo + m0 * N + n0,
+                                   dso32 + m0 * (N / kBlock) + n0 / kBlock, (int)mm, (int)nn, K, tiles_m, N,
+                                   (int64_t)0, 0, sc.gps);
             }
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
@@ -388,13 +486,23 @@ hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uin
                       const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
                       const DeviceInfo &dev, hipStream_t stream)
 {
-    return run_tiles(false, qa, ds, M, qs, sm, N, K, y, nullptr, workspace, dev.num_cus, stream);
+    return run_tiles(kOutY, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace, dev.num_cus,
+                     stream);
+}
+
+hipError_t launch_mmq_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                           const uint16_t *sm, int64_t N, int K, int8_t *qo, uint16_t *dso,
+                           void *workspace, const DeviceInfo &dev, hipStream_t stream)
+{
+    return run_tiles(kOutQ8, qa, ds, M, qs, sm, N, K, nullptr, nullptr, qo, dso, workspace, dev.num_cus,
+                     stream);
 }
 
 hipError_t launch_block_dots(const int8_t *qa, int64_t M, const uint8_t *qs, int64_t N, int K,
                              int32_t *idot, const DeviceInfo &dev, hipStream_t stream)
 {
-    return run_tiles(true, qa, nullptr, M, qs, nullptr, N, K, nullptr, idot, nullptr, dev.num_cus, stream);
+    return run_tiles(kOutDots, qa, nullptr, M, qs, nullptr, N, K, nullptr, idot, nullptr, nullptr, nullptr,
+                     dev.num_cus, stream);
 }
 
 }  // namespace q4mi

@@ -144,6 +144,26 @@ int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *
                                           (hipStream_t)stream));
 }
 
+int q4_mmq_gemm_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                     const uint16_t *sm, int64_t N, int64_t K, int8_t *qa_out, uint16_t *ds_out,
+                     void *workspace, size_t ws_bytes, void *stream)
+{
+    if (M < 0 || M > Q4_MAX_M_MMQ || N < 0 || N > Q4_MAX_N || N % 32 != 0 || !valid_k(K, 256))
+        return Q4_ERR_ARG;
+    if (M == 0 || N == 0) return Q4_OK;
+    if (!qa || !ds || !qs || !sm || !qa_out || !ds_out) return Q4_ERR_ARG;
+    if (!aligned(qa, 16) || !aligned(ds, 4) || !aligned(qs, 16) || !aligned(sm, 4) ||
+        !aligned(qa_out, 4) || !aligned(ds_out, 4))
+        return Q4_ERR_ALIGN;
+    const size_t need = q4mi::mmq_workspace_bytes(M, N, K);
+    if (need > 0 && (!workspace || ws_bytes < need)) return Q4_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return Q4_ERR_ALIGN;
+    const DeviceInfo *dev = nullptr;
+    if (int rc = current_device(&dev)) return rc;
+    return launch_status(q4mi::launch_mmq_q8_1(qa, ds, M, qs, sm, N, (int)K, qa_out, ds_out, workspace,
+                                               *dev, (hipStream_t)stream));
+}
+
 int q4_mmq_block_dots(const int8_t *qa, int64_t M, const uint8_t *qs, int64_t N, int64_t K,
                       int32_t *idot, void *stream)
 {

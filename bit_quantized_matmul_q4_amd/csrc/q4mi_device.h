@@ -58,6 +58,25 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
 
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
+// Q8_1 decisions for one block of 32 values, in IEEE fp32 with correctly
+// rounded division (every kernel that produces Q8_1 uses these, so their codes
+// agree bit for bit): d16 = fp16(amax / 127); a = clamp(rint(x / d), -127, 127)
+// (0 when d is 0); s16 = fp16(d * sum a), the product exact in fp32.
+__device__ __forceinline__ uint16_t q8_1_scale(float amax) { return f32_to_f16_bits(__fdiv_rn(amax, 127.0f)); }
+
+__device__ __forceinline__ int q8_1_code(float x, float df)
+{
+    if (df == 0.0f) return 0;
+    const float r = rintf(__fdiv_rn(x, df));
+    return r < -127.0f ? -127 : (r > 127.0f ? 127 : (int)r);
+}
+
+__device__ __forceinline__ uint32_t q8_1_ds(uint16_t d16, float df, int sum)
+{
+    const uint16_t s16 = f32_to_f16_bits(__fmul_rn(df, (float)sum));
+    return (uint32_t)d16 | ((uint32_t)s16 << 16);
+}
+
 // Raw buffer loads.  The descriptor carries the buffer size; a load whose
 // bytes fall outside it returns zeros, so edge rows need no branch (a branch
 // around a load makes the compiler wait for every outstanding load).

@@ -76,18 +76,14 @@ __global__ __launch_bounds__(256) void k_q8_1_quantize(const float *__restrict__
         amax = fmaxf(amax, __shfl_xor(amax, 1));
         amax = fmaxf(amax, __shfl_xor(amax, 2));
         amax = fmaxf(amax, __shfl_xor(amax, 4));
-        const uint16_t d16 = f32_to_f16_bits(__fdiv_rn(amax, 127.0f));
+        const uint16_t d16 = q8_1_scale(amax);
         const float df = f16_bits_to_f32(d16);
         const float e[4] = {v.x, v.y, v.z, v.w};
         uint32_t packed = 0;
         int sum = 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            int a = 0;
-            if (df != 0.0f) {
-                const float r = rintf(__fdiv_rn(e[t], df));
-                a = r < -127.0f ? -127 : (r > 127.0f ? 127 : (int)r);
-            }
+            const int a = q8_1_code(e[t], df);
             sum += a;
             packed |= ((uint32_t)a & 0xFFu) << (8 * t);
         }
@@ -95,10 +91,7 @@ __global__ __launch_bounds__(256) void k_q8_1_quantize(const float *__restrict__
         sum += __shfl_xor(sum, 2);
         sum += __shfl_xor(sum, 4);
         reinterpret_cast<uint32_t *>(qa)[i] = packed;
-        if ((i & 7) == 0) {
-            const uint16_t s16 = f32_to_f16_bits(__fmul_rn(df, (float)sum));  // exact product
-            ds[i >> 3] = (uint32_t)d16 | ((uint32_t)s16 << 16);
-        }
+        if ((i & 7) == 0) ds[i >> 3] = q8_1_ds(d16, df, sum);
     }
 }
 

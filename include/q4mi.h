@@ -169,6 +169,27 @@ int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *
                 size_t ws_bytes, void *stream);
 
 /*
+ * q4_mmq_gemm_q8_1 -- q4_mmq_gemm whose epilogue hands its result on as Q8_1
+ * activations for a following MMQ layer instead of writing fp32: the
+ * quantization step that the hipfire MMQ note runs ahead of the prefill GEMM
+ * ("list of changes": activations pre-quantized to Q8_1 in MMQ layout), moved
+ * into the producing GEMM.  The output is exactly
+ *     q8_1_quantize(q4_mmq_gemm(qa, ds, qs, sm))
+ * bit for bit: the same fp32 y, quantized along n in blocks of 32 with the
+ * same decisions (d = fp16(amax/127), a = clamp(rint(y/d), -127, 127),
+ * s = fp16(d * sum a)).  N must be a multiple of 32.
+ *   qa, ds, qs, sm: as for q4_mmq_gemm.  qa_out: device i8 [M][N], 4-byte
+ *   aligned.  ds_out: device u16 [M][N/32][2] = (d, s), 4-byte aligned.
+ *   workspace: at least q4_mmq_workspace_bytes(M, N, K) bytes (the same
+ *   split partials as q4_mmq_gemm), 16-byte aligned, NULL allowed when 0.
+ * Errors: Q4_ERR_ARG (also N not a multiple of 32), Q4_ERR_ALIGN,
+ * Q4_ERR_WORKSPACE, Q4_ERR_ARCH, Q4_ERR_DEVICE, Q4_ERR_LAUNCH.
+ */
+int q4_mmq_gemm_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                     const uint16_t *sm, int64_t N, int64_t K, int8_t *qa_out, uint16_t *ds_out,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * q4_mmq_block_dots -- the integer core of q4_mmq_gemm on its own, for
  * checking it bit-exactly (the "keep-quant integer core" the vllm.cpp TG150
  * campaign keeps bit-exact against the CPU, pull request 4, "Design"):

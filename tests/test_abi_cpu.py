@@ -125,3 +125,15 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libq4mi.so")
     with pytest.raises(ImportError):
         _lib.lib()
+
+
+def test_mmq_q8_1_output_argument_checks():
+    L = q4.lib()
+    fn = L.q4_mmq_gemm_q8_1
+    # N must be a multiple of 32 (Q8_1 blocks along n)
+    assert fn(FAKE, FAKE, 4, FAKE, FAKE, 48, 256, FAKE, FAKE, NULL, 0, NULL) == ARG
+    assert fn(FAKE, FAKE, 4, FAKE, FAKE, 64, 100, FAKE, FAKE, NULL, 0, NULL) == ARG
+    # empty problems are no-ops; missing outputs are argument errors
+    assert fn(NULL, NULL, 0, NULL, NULL, 64, 256, NULL, NULL, NULL, 0, NULL) == 0
+    assert fn(FAKE, FAKE, 4, FAKE, FAKE, 64, 256, NULL, FAKE, NULL, 0, NULL) == ARG
+    assert fn(FAKE, FAKE, 4, FAKE, FAKE, 64, 256, FAKE, NULL, NULL, 0, NULL) == ARG

@@ -343,6 +343,26 @@ def test_mmq_long_k(q4, orc):
     mmq_check(q4, orc, 130, 100, 65792, 77, True, "mmq long K")
 
 
+@pytest.mark.parametrize("M,N,K,seed", [(100, 224, 512, 61), (100, 224, 2048, 62), (512, 9216, 2560, 0)])
+def test_mmq_q8_1_output_bit_exact(q4, orc, M, N, K, seed):
+    # the Q8_1-producing epilogue equals quantizing the fp32 GEMM result, bit
+    # for bit (K = 2048 at 2 tiles takes the K-split path, whose sum pass
+    # quantizes); and the oracle's quantizer on that fp32 result agrees too
+    say("mmq -> Q8_1 M=%d N=%d K=%d" % (M, N, K))
+    W, x = wl.mmq_case(seed, M, N, K, True)
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    qo, dso = q4.q4_mmq_gemm_q8_1(qa, ds, qs, sm)
+    y = q4.q4_mmq_gemm(qa, ds, qs, sm)
+    qr, dsr = q4.q8_1_quantize(y)
+    assert torch.equal(qo, qr)
+    assert torch.equal(dso.view(torch.int16), dsr.view(torch.int16))
+    rows = slice(None) if M <= 100 else slice(0, 64)
+    oq, ods = orc.q8_1_quantize(y[rows].cpu().numpy())
+    assert np.array_equal(qo[rows].cpu().numpy(), oq)
+    assert np.array_equal(dso[rows].cpu().view(torch.int16).numpy().view(np.uint16), ods)
+
+
 def test_mmq_m1_matches_gemv_on_dequantized_row(q4, orc):
     say("mmq M=1 vs gemv on the dequantized Q8_1 row")
     W, x = wl.mmq_case(5, 1, 777, 2560)
