@@ -151,7 +151,7 @@ static void parallel_rows(int64_t n, range_fn fn, void *ctx)
 }
 
 /* ------------------------------------------------------------------ */
-/* 4-bit group-256 weights                                             */
+/* 4-bit weights, groups of 256 (and of 32)                            */
 /* ------------------------------------------------------------------ */
 /* Layout (the project's reading; the pages name the format only):
  *   qs  u8  [N][K/2]   group g of row n occupies bytes [128 g, 128 g + 128).
@@ -161,23 +161,30 @@ static void parallel_rows(int64_t n, range_fn fn, void *ctx)
  *                       element 32 j + i + 16 in its high nibble.
  *   sm  f16 [N][K/256][2]   (scale, minimum) per group.
  * Dequantized weight: w' = scale * q + minimum, with scale and minimum taken
- * from their fp16 values. */
+ * from their fp16 values.
+ * The group-32 variant (the *_g functions with group = 32) keeps qs exactly
+ * as above and carries one (scale, minimum) pair per 32 weights,
+ * sm f16 [N][K/32][2]; packing and dequantization are the same steps over
+ * groups of 32. */
 #define GROUP 256
 #define BLOCK 32
 
-/* byte offset and nibble (0 = low, 1 = high) of element k of one row */
+/* byte offset and nibble (0 = low, 1 = high) of element k of one row; the
+ * layout is the same for both group sizes (a group of 256 is eight runs of 32) */
 static inline void code_position(int64_t k, int64_t *byte, int *hi)
 {
-    int64_t g = k / GROUP, r = k % GROUP;
     if (g_mutation == MUT_NIBBLE_SEQUENTIAL) {
-        *byte = g * (GROUP / 2) + r / 2;
-        *hi = (int)(r & 1);
+        *byte = k / 2;
+        *hi = (int)(k & 1);
         return;
     }
-    int64_t j = r / BLOCK, i = r % BLOCK;
-    *byte = g * (GROUP / 2) + j * 16 + (i & 15);
+    int64_t j = k / BLOCK, i = k % BLOCK;
+    *byte = j * 16 + (i & 15);
     *hi = i >= 16;
 }
+
+/* the two group sizes of (scale, minimum) pairs: 256 and 32 weights */
+static inline int valid_group(int64_t group) { return group == GROUP || group == BLOCK; }
 
 static inline int read_code(const uint8_t *row, int64_t k)
 {
@@ -187,22 +194,22 @@ static inline int read_code(const uint8_t *row, int64_t k)
 }
 
 typedef struct {
-    const float *W; int64_t K; uint8_t *qs; uint16_t *sm;
+    const float *W; int64_t K; uint8_t *qs; uint16_t *sm; int64_t group;
 } pack_ctx;
 
 static void pack_rows(void *p, int64_t lo, int64_t hi)
 {
     pack_ctx *c = (pack_ctx *)p;
-    const int64_t K = c->K, G = K / GROUP;
+    const int64_t K = c->K, GS = c->group, G = K / GS;
     for (int64_t n = lo; n < hi; ++n) {
         const float *w = c->W + n * K;
         uint8_t *row = c->qs + n * (K / 2);
         uint16_t *sm = c->sm + n * G * 2;
         memset(row, 0, (size_t)(K / 2));
         for (int64_t g = 0; g < G; ++g) {
-            const float *wg = w + g * GROUP;
+            const float *wg = w + g * GS;
             float mn = wg[0], mx = wg[0];
-            for (int k = 1; k < GROUP; ++k) {
+            for (int k = 1; k < GS; ++k) {
                 if (wg[k] < mn) mn = wg[k];
                 if (wg[k] > mx) mx = wg[k];
             }
@@ -216,7 +223,7 @@ static void pack_rows(void *p, int64_t lo, int64_t hi)
             float sf = orc_f16_to_f32(s16), mf = orc_f16_to_f32(m16);
             sm[2 * g] = s16;
             sm[2 * g + 1] = m16;
-            for (int k = 0; k < GROUP; ++k) {
+            for (int k = 0; k < GS; ++k) {
                 int q = 0;
                 if (sf != 0.0f) {
                     float t = (wg[k] - mf) / sf;          /* fp32 sub, fp32 divide */
@@ -224,28 +231,34 @@ static void pack_rows(void *p, int64_t lo, int64_t hi)
                     q = r < 0.0f ? 0 : (r > 15.0f ? 15 : (int)r);
                 }
                 int64_t b; int h;
-                code_position(g * GROUP + k, &b, &h);
+                code_position(g * GS + k, &b, &h);
                 row[b] |= (uint8_t)(h ? (q << 4) : q);
             }
         }
     }
 }
 
-/* Pack W [N][K] fp32 into qs/sm.  Returns 0, or -1 on bad arguments. */
-int orc_q4_pack(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm)
+/* Pack W [N][K] fp32 into qs/sm with one (scale, minimum) pair per group of
+ * `group` (256 or 32) weights along K.  Returns 0, or -1 on bad arguments. */
+int orc_q4_pack_g(const float *W, int64_t N, int64_t K, int64_t group, uint8_t *qs, uint16_t *sm)
 {
-    if (!W || !qs || !sm || N < 0 || K <= 0 || K % GROUP) return -1;
-    pack_ctx c = {W, K, qs, sm};
+    if (!W || !qs || !sm || N < 0 || K <= 0 || !valid_group(group) || K % GROUP) return -1;
+    pack_ctx c = {W, K, qs, sm, group};
     parallel_rows(N, pack_rows, &c);
     return 0;
 }
 
-/* Exact dequantization of one row into fp64. */
-static void dequant_row(const uint8_t *row, const uint16_t *sm, int64_t K, double *out)
+int orc_q4_pack(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm)
 {
-    const int64_t G = K / GROUP;
+    return orc_q4_pack_g(W, N, K, GROUP, qs, sm);
+}
+
+/* Exact dequantization of one row into fp64. */
+static void dequant_row(const uint8_t *row, const uint16_t *sm, int64_t K, int64_t GS, double *out)
+{
+    const int64_t G = K / GS;
     for (int64_t k = 0; k < K; ++k) {
-        int64_t g = k / GROUP;
+        int64_t g = k / GS;
         if (g_mutation == MUT_GROUP_OFF_BY_ONE && g + 1 < G) g += 1;
         double s = (double)orc_f16_to_f32(sm[2 * g]);
         double m = (double)orc_f16_to_f32(sm[2 * g + 1]);
@@ -254,12 +267,18 @@ static void dequant_row(const uint8_t *row, const uint16_t *sm, int64_t K, doubl
     }
 }
 
+int orc_q4_dequant_g(const uint8_t *qs, const uint16_t *sm, int64_t N, int64_t K, int64_t group,
+                     double *Wd)
+{
+    if (!qs || !sm || !Wd || N < 0 || K <= 0 || !valid_group(group) || K % GROUP) return -1;
+    for (int64_t n = 0; n < N; ++n)
+        dequant_row(qs + n * (K / 2), sm + n * (K / group) * 2, K, group, Wd + n * K);
+    return 0;
+}
+
 int orc_q4_dequant(const uint8_t *qs, const uint16_t *sm, int64_t N, int64_t K, double *Wd)
 {
-    if (!qs || !sm || !Wd || N < 0 || K <= 0 || K % GROUP) return -1;
-    for (int64_t n = 0; n < N; ++n)
-        dequant_row(qs + n * (K / 2), sm + n * (K / GROUP) * 2, K, Wd + n * K);
-    return 0;
+    return orc_q4_dequant_g(qs, sm, N, K, GROUP, Wd);
 }
 
 /* Unpack the 4-bit codes of W (as integers 0..15) into codes [N][K]. */
@@ -319,7 +338,7 @@ int orc_q8_1_quantize(const float *x, int64_t M, int64_t K, int8_t *qa, uint16_t
 /* ------------------------------------------------------------------ */
 typedef struct {
     const float *x; int64_t M; const uint8_t *qs; const uint16_t *sm;
-    int64_t N, K; double *y;
+    int64_t N, K; double *y; int64_t group;
 } gemv_ctx;
 
 static void gemv_rows(void *p, int64_t lo, int64_t hi)
@@ -332,14 +351,14 @@ static void gemv_rows(void *p, int64_t lo, int64_t hi)
             /* planted mistake: weight element (n, k) read from row k, column n */
             for (int64_t k = 0; k < K; ++k) {
                 int64_t rn = k % c->N, rk = n % K;
-                int64_t g = rk / GROUP;
+                int64_t g = rk / c->group;
                 const uint8_t *row = c->qs + rn * (K / 2);
-                const uint16_t *sm = c->sm + rn * (K / GROUP) * 2;
+                const uint16_t *sm = c->sm + rn * (K / c->group) * 2;
                 w[k] = (double)orc_f16_to_f32(sm[2 * g]) * read_code(row, rk) +
                        (double)orc_f16_to_f32(sm[2 * g + 1]);
             }
         } else {
-            dequant_row(c->qs + n * (K / 2), c->sm + n * (K / GROUP) * 2, K, w);
+            dequant_row(c->qs + n * (K / 2), c->sm + n * (K / c->group) * 2, K, c->group, w);
         }
         for (int64_t m = 0; m < c->M; ++m) {
             const float *xm = c->x + m * K;
@@ -351,13 +370,19 @@ static void gemv_rows(void *p, int64_t lo, int64_t hi)
     free(w);
 }
 
+int orc_q4_gemv_g(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm,
+                  int64_t N, int64_t K, int64_t group, double *y)
+{
+    if (!x || !qs || !sm || !y || M < 0 || N < 0 || K <= 0 || !valid_group(group) || K % GROUP) return -1;
+    gemv_ctx c = {x, M, qs, sm, N, K, y, group};
+    parallel_rows(N, gemv_rows, &c);
+    return 0;
+}
+
 int orc_q4_gemv(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm,
                 int64_t N, int64_t K, double *y)
 {
-    if (!x || !qs || !sm || !y || M < 0 || N < 0 || K <= 0 || K % GROUP) return -1;
-    gemv_ctx c = {x, M, qs, sm, N, K, y};
-    parallel_rows(N, gemv_rows, &c);
-    return 0;
+    return orc_q4_gemv_g(x, M, qs, sm, N, K, GROUP, y);
 }
 
 /* ------------------------------------------------------------------ */
@@ -392,6 +417,7 @@ typedef struct {
     const int8_t *qa; const uint16_t *ds; int64_t M;
     const uint8_t *qs; const uint16_t *sm; int64_t N, K; double *y;
     const double *xd;   /* dequantized activations [M][K] */
+    int64_t group;
 } mmq_ctx;
 
 static void mmq_rows(void *p, int64_t lo, int64_t hi)
@@ -400,7 +426,7 @@ static void mmq_rows(void *p, int64_t lo, int64_t hi)
     const int64_t K = c->K;
     double *w = (double *)malloc(sizeof(double) * (size_t)K);
     for (int64_t n = lo; n < hi; ++n) {
-        dequant_row(c->qs + n * (K / 2), c->sm + n * (K / GROUP) * 2, K, w);
+        dequant_row(c->qs + n * (K / 2), c->sm + n * (K / c->group) * 2, K, c->group, w);
         for (int64_t m = 0; m < c->M; ++m) {
             const double *xm = c->xd + m * K;
             double acc = 0.0;
@@ -425,15 +451,22 @@ int orc_q8_1_dequant(const int8_t *qa, const uint16_t *ds, int64_t M, int64_t K,
     return 0;
 }
 
-int orc_q4_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
-               const uint16_t *sm, int64_t N, int64_t K, double *y)
+int orc_q4_mmq_g(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                 const uint16_t *sm, int64_t N, int64_t K, int64_t group, double *y)
 {
-    if (!qa || !ds || !qs || !sm || !y || M < 0 || N < 0 || K <= 0 || K % GROUP) return -1;
+    if (!qa || !ds || !qs || !sm || !y || M < 0 || N < 0 || K <= 0 || !valid_group(group) || K % GROUP)
+        return -1;
     double *xd = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
     if (!xd) return -2;
     orc_q8_1_dequant(qa, ds, M, K, xd);
-    mmq_ctx c = {qa, ds, M, qs, sm, N, K, y, xd};
+    mmq_ctx c = {qa, ds, M, qs, sm, N, K, y, xd, group};
     parallel_rows(N, mmq_rows, &c);
     free(xd);
     return 0;
+}
+
+int orc_q4_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+               const uint16_t *sm, int64_t N, int64_t K, double *y)
+{
+    return orc_q4_mmq_g(qa, ds, M, qs, sm, N, K, GROUP, y);
 }

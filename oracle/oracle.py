@@ -6,12 +6,12 @@ does.  It loads ``liboracle.so`` built from ``oracle.c`` by ``build()`` below
 (gcc, no GPU code) and marshals numpy arrays into the plain C calls.
 
 Every function returns fresh numpy arrays:
-    q4_pack(W)                -> (qs u8 [N][K/2], sm u16 [N][K/256][2])
+    q4_pack(W, group=256)     -> (qs u8 [N][K/2], sm u16 [N][K/group][2]); group 256 or 32
     q4_dequant(qs, sm, K)     -> fp64 [N][K]
     q4_codes(qs, K)           -> u8 [N][K] codes 0..15
     q8_1_quantize(x)          -> (qa i8 [M][K], ds u16 [M][K/32][2])
     q8_1_dequant(qa, ds)      -> fp64 [M][K]
-    q4_gemv(x, qs, sm, K)     -> fp64 [M][N]
+    q4_gemv(x, qs, sm, K)     -> fp64 [M][N]   (the weight functions take group= too)
     q4_block_dots(qa, qs, K)  -> i32 [M][N][K/32]
     q4_mmq(qa, ds, qs, sm, K) -> fp64 [M][N]
     f32_to_f16(a) / f16_to_f32(h) elementwise IEEE binary16 conversion
@@ -64,6 +64,10 @@ def _load():
         "orc_f32_to_f16": ([ctypes.c_float], ctypes.c_uint16),
         "orc_f16_to_f32": ([ctypes.c_uint16], ctypes.c_float),
         "orc_q4_pack": ([P, I64, I64, P, P], ctypes.c_int),
+        "orc_q4_pack_g": ([P, I64, I64, I64, P, P], ctypes.c_int),
+        "orc_q4_dequant_g": ([P, P, I64, I64, I64, P], ctypes.c_int),
+        "orc_q4_gemv_g": ([P, I64, P, P, I64, I64, I64, P], ctypes.c_int),
+        "orc_q4_mmq_g": ([P, P, I64, P, P, I64, I64, I64, P], ctypes.c_int),
         "orc_q4_dequant": ([P, P, I64, I64, P], ctypes.c_int),
         "orc_q4_codes": ([P, I64, I64, P], ctypes.c_int),
         "orc_q8_1_quantize": ([P, I64, I64, P, P], ctypes.c_int),
@@ -136,21 +140,22 @@ def f16_to_f32(h):
     return out
 
 
-def q4_pack(W):
+def q4_pack(W, group=GROUP):
+    """group = 256 (the main format) or 32 (one scale/minimum pair per 32 weights)."""
     W = _c(W, np.float32)
     N, K = W.shape
     qs = np.empty((N, K // 2), dtype=np.uint8)
-    sm = np.empty((N, K // GROUP, 2), dtype=np.uint16)
-    _check(_load().orc_q4_pack(_ptr(W), N, K, _ptr(qs), _ptr(sm)), "q4_pack")
+    sm = np.empty((N, K // group, 2), dtype=np.uint16)
+    _check(_load().orc_q4_pack_g(_ptr(W), N, K, group, _ptr(qs), _ptr(sm)), "q4_pack")
     return qs, sm
 
 
-def q4_dequant(qs, sm, K):
+def q4_dequant(qs, sm, K, group=GROUP):
     qs = _c(qs, np.uint8)
     sm = _c(sm, np.uint16)
     N = qs.shape[0]
     out = np.empty((N, K), dtype=np.float64)
-    _check(_load().orc_q4_dequant(_ptr(qs), _ptr(sm), N, K, _ptr(out)), "q4_dequant")
+    _check(_load().orc_q4_dequant_g(_ptr(qs), _ptr(sm), N, K, group, _ptr(out)), "q4_dequant")
     return out
 
 
@@ -180,14 +185,14 @@ def q8_1_dequant(qa, ds):
     return out
 
 
-def q4_gemv(x, qs, sm, K):
+def q4_gemv(x, qs, sm, K, group=GROUP):
     x = _c(x, np.float32)
     qs = _c(qs, np.uint8)
     sm = _c(sm, np.uint16)
     M, N = x.shape[0], qs.shape[0]
-    assert x.shape[1] == K and qs.shape[1] == K // 2
+    assert x.shape[1] == K and qs.shape[1] == K // 2 and sm.shape[1] == K // group
     y = np.empty((M, N), dtype=np.float64)
-    _check(_load().orc_q4_gemv(_ptr(x), M, _ptr(qs), _ptr(sm), N, K, _ptr(y)), "q4_gemv")
+    _check(_load().orc_q4_gemv_g(_ptr(x), M, _ptr(qs), _ptr(sm), N, K, group, _ptr(y)), "q4_gemv")
     return y
 
 
@@ -200,12 +205,13 @@ def q4_block_dots(qa, qs, K):
     return out
 
 
-def q4_mmq(qa, ds, qs, sm, K):
+def q4_mmq(qa, ds, qs, sm, K, group=GROUP):
     qa = _c(qa, np.int8)
     ds = _c(ds, np.uint16)
     qs = _c(qs, np.uint8)
     sm = _c(sm, np.uint16)
     M, N = qa.shape[0], qs.shape[0]
+    assert sm.shape[1] == K // group
     y = np.empty((M, N), dtype=np.float64)
-    _check(_load().orc_q4_mmq(_ptr(qa), _ptr(ds), M, _ptr(qs), _ptr(sm), N, K, _ptr(y)), "q4_mmq")
+    _check(_load().orc_q4_mmq_g(_ptr(qa), _ptr(ds), M, _ptr(qs), _ptr(sm), N, K, group, _ptr(y)), "q4_mmq")
     return y

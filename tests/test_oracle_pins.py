@@ -40,24 +40,25 @@ def _f16(v):
     return np.float32(np.float16(v))
 
 
-def grid_weights(rng, N, K, with_ends=True):
+def grid_weights(rng, N, K, with_ends=True, group=256):
     """W exactly on the 4-bit grid: W[n, k] = mf + sf * c with fp16-exact
-    (mf, sf) per group.  Returns (W fp32, codes, sf per group, mf per group).
-    With ``with_ends`` every group contains codes 0 and 15, so the group min
-    and max are mf and mf + 15 sf and packing must return exactly c."""
-    G = K // 256
+    (mf, sf) per group of ``group`` weights.  Returns (W fp32, codes, sf per
+    group, mf per group).  With ``with_ends`` every group contains codes 0 and
+    15, so the group min and max are mf and mf + 15 sf and packing must return
+    exactly c."""
+    G = K // group
     codes = rng.integers(0, 16, size=(N, K)).astype(np.int64)
     if with_ends:
         for n in range(N):
             for g in range(G):
-                i0, i1 = rng.choice(256, size=2, replace=False)
-                codes[n, g * 256 + i0] = 0
-                codes[n, g * 256 + i1] = 15
+                i0, i1 = rng.choice(group, size=2, replace=False)
+                codes[n, g * group + i0] = 0
+                codes[n, g * group + i1] = 15
     # scales: small integers times powers of two, all exact in fp16 and fp32
     sf = (rng.integers(1, 32, size=(N, G)) * 2.0 ** rng.integers(-12, -4, size=(N, G)))
     mf = (rng.integers(-64, 64, size=(N, G)) * 2.0 ** rng.integers(-10, -5, size=(N, G)))
-    sfk = np.repeat(sf, 256, axis=1)
-    mfk = np.repeat(mf, 256, axis=1)
+    sfk = np.repeat(sf, group, axis=1)
+    mfk = np.repeat(mf, group, axis=1)
     W = mfk + sfk * codes
     assert np.all(W.astype(np.float32).astype(np.float64) == W)
     return W.astype(np.float32), codes, sf, mf
@@ -375,6 +376,88 @@ def pin_mmq_unit_scales_sum_block_dots(o):
     y = o.q4_mmq(qa, ds, qs, sm, 512)
     dots = o.q4_block_dots(qa, qs, 512).sum(axis=2)
     assert np.array_equal(y, dots.astype(np.float64))
+
+
+# ------------------------------------------------------------ group 32 ----
+# The group-32 variant keeps the code bytes and carries a (scale, minimum)
+# pair per 32 weights.
+
+def pin_g32_closed_form(o):
+    rng = np.random.default_rng(21)
+    W, codes, sf, mf = grid_weights(rng, 5, 512, group=32)
+    qs, sm = o.q4_pack(W, group=32)
+    assert sm.shape == (5, 16, 2)
+    assert np.array_equal(o.q4_codes(qs, 512), codes), "codes of an exact grid"
+    assert np.array_equal(o.f16_to_f32(sm[..., 0]), sf.astype(np.float32))
+    assert np.array_equal(o.f16_to_f32(sm[..., 1]), mf.astype(np.float32))
+    assert np.array_equal(o.q4_dequant(qs, sm, 512, group=32), W.astype(np.float64))
+
+
+def pin_g32_same_bytes_as_g256(o):
+    # a group-256 grid whose every run of 32 holds codes 0 and 15: both group
+    # sizes find the same codes, so the code bytes agree and every run of 32
+    # carries its group's pair
+    rng = np.random.default_rng(22)
+    W, codes, sf, mf = grid_weights(rng, 4, 512)
+    for n in range(4):
+        for r in range(16):
+            i0, i1 = rng.choice(32, size=2, replace=False)
+            codes[n, 32 * r + i0], codes[n, 32 * r + i1] = 0, 15
+    W = (np.repeat(mf, 256, axis=1) + np.repeat(sf, 256, axis=1) * codes).astype(np.float32)
+    qs256, sm256 = o.q4_pack(W)
+    qs32, sm32 = o.q4_pack(W, group=32)
+    assert np.array_equal(qs32, qs256)
+    assert np.array_equal(sm32, np.repeat(sm256, 8, axis=1))
+
+
+def pin_g32_nearest_level_and_constant_run(o):
+    rng = np.random.default_rng(23)
+    W = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    W[2, 64:96] = np.float32(0.01)  # one constant run of 32
+    qs, sm = o.q4_pack(W, group=32)
+    c = o.q4_codes(qs, 256)
+    for n in range(8):
+        for g in range(8):
+            s = float(o.f16_to_f32(sm[n, g, 0]))
+            m = float(o.f16_to_f32(sm[n, g, 1]))
+            levels = m + s * np.arange(16)
+            w = W[n, g * 32:(g + 1) * 32].astype(np.float64)
+            dist = np.abs(w[:, None] - levels[None, :])
+            got = dist[np.arange(32), c[n, g * 32:(g + 1) * 32]]
+            assert np.all(got <= dist.min(axis=1) + 1e-6 * max(s, 1e-30)), "not the nearest level"
+    assert sm[2, 2, 0] == 0 and np.all(c[2, 64:96] == 0)
+    assert np.all(o.q4_dequant(qs, sm, 256, group=32)[2, 64:96] == np.float64(_f16(0.01)))
+
+
+def pin_g32_gemv_and_mmq_exact_grid(o):
+    rng = np.random.default_rng(24)
+    W, _, _, _ = grid_weights(rng, 7, 768, group=32)
+    qs, sm = o.q4_pack(W, group=32)
+    x = rng.standard_normal((3, 768)).astype(np.float32)
+    y = o.q4_gemv(x, qs, sm, 768, group=32)
+    want = x.astype(np.float64) @ W.astype(np.float64).T
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    ks = [0, 31, 32, 33, 100, 767]
+    e = np.zeros((len(ks), 768), dtype=np.float32)
+    e[np.arange(len(ks)), ks] = 1.0
+    assert np.array_equal(o.q4_gemv(e, qs, sm, 768, group=32), W[:, ks].T.astype(np.float64))
+    xg, _, _ = grid_activations(rng, 4, 768)
+    qa, ds = o.q8_1_quantize(xg)
+    y = o.q4_mmq(qa, ds, qs, sm, 768, group=32)
+    want = xg.astype(np.float64) @ W.astype(np.float64).T
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def pin_g32_equal_runs_reduce_to_g256(o):
+    # pairs repeated over the eight runs of each group give the group-256 results
+    rng = np.random.default_rng(25)
+    W = (rng.standard_normal((9, 512)) * 0.02).astype(np.float32)
+    qs, sm = o.q4_pack(W)
+    sm32 = np.repeat(sm, 8, axis=1)
+    x = rng.standard_normal((2, 512)).astype(np.float32)
+    assert np.array_equal(o.q4_gemv(x, qs, sm32, 512, group=32), o.q4_gemv(x, qs, sm, 512))
+    qa, ds = o.q8_1_quantize(x)
+    assert np.array_equal(o.q4_mmq(qa, ds, qs, sm32, 512, group=32), o.q4_mmq(qa, ds, qs, sm, 512))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
