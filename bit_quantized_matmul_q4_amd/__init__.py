@@ -10,12 +10,15 @@ from ._lib import (  # noqa: F401
     lib,
     q4_abi_version,
     q4_gemv,
+    q4_gemv_g32,
+    q4_gemv_g32_workspace_bytes,
     q4_gemv_workspace_bytes,
     q4_mmq_block_dots,
     q4_mmq_gemm,
     q4_mmq_gemm_q8_1,
     q4_mmq_workspace_bytes,
     q4_pack,
+    q4_pack_g32,
     q8_1_quantize,
     strerror,
 )

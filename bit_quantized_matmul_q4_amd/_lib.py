@@ -27,6 +27,7 @@ GEMV_MAX_M = 16
 SYMBOLS = [
     "q4_abi_version", "q4_strerror", "q4_pack", "q8_1_quantize", "q4_gemv_workspace_bytes",
     "q4_gemv", "q4_mmq_workspace_bytes", "q4_mmq_gemm", "q4_mmq_gemm_q8_1", "q4_mmq_block_dots",
+    "q4_pack_g32", "q4_gemv_g32_workspace_bytes", "q4_gemv_g32",
 ]
 
 _lib = None
@@ -59,6 +60,9 @@ def lib():
         "q4_mmq_gemm": ([P, P, I64, P, P, I64, I64, P, P, SZ, P], I),
         "q4_mmq_gemm_q8_1": ([P, P, I64, P, P, I64, I64, P, P, P, SZ, P], I),
         "q4_mmq_block_dots": ([P, I64, P, I64, I64, P, P], I),
+        "q4_pack_g32": ([P, I64, I64, P, P, P], I),
+        "q4_gemv_g32_workspace_bytes": ([I64, I64, I64], SZ),
+        "q4_gemv_g32": ([P, I64, P, P, I64, I64, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -161,6 +165,40 @@ def q4_gemv(x, qs, sm, y=None, workspace=None, stream=None):
     ws, wsb = _workspace(q4_gemv_workspace_bytes(M, N, K), workspace, x.device)
     _check(lib().q4_gemv(_ptr(x), M, _ptr(qs), _ptr(sm), N, K, _ptr(y), _ptr(ws), wsb,
                          _stream(stream, x)), "q4_gemv")
+    return y
+
+
+def q4_pack_g32(W, qs=None, sm=None, stream=None):
+    """W fp32 [N][K] -> (qs uint8 [N][K/2], sm float16 [N][K/32][2]): group-32 pairs."""
+    N, K = W.shape
+    _need(W, torch.float32, (N, K), "W")
+    if qs is None:
+        qs = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    if sm is None:
+        sm = torch.empty((N, K // 32, 2), dtype=torch.float16, device=W.device)
+    _need(qs, torch.uint8, (N, K // 2), "qs")
+    _need(sm, torch.float16, (N, K // 32, 2), "sm")
+    _check(lib().q4_pack_g32(_ptr(W), N, K, _ptr(qs), _ptr(sm), _stream(stream, W)), "q4_pack_g32")
+    return qs, sm
+
+
+def q4_gemv_g32_workspace_bytes(M, N, K):
+    return lib().q4_gemv_g32_workspace_bytes(int(M), int(N), int(K))
+
+
+def q4_gemv_g32(x, qs, sm, y=None, workspace=None, stream=None):
+    """q4_gemv on group-32 weights (sm float16 [N][K/32][2])."""
+    M, K = x.shape
+    N = qs.shape[0]
+    _need(x, torch.float32, (M, K), "x")
+    _need(qs, torch.uint8, (N, K // 2), "qs")
+    _need(sm, torch.float16, (N, K // 32, 2), "sm")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(y, torch.float32, (M, N), "y")
+    ws, wsb = _workspace(q4_gemv_g32_workspace_bytes(M, N, K), workspace, x.device)
+    _check(lib().q4_gemv_g32(_ptr(x), M, _ptr(qs), _ptr(sm), N, K, _ptr(y), _ptr(ws), wsb,
+                             _stream(stream, x)), "q4_gemv_g32")
     return y
 
 

@@ -154,7 +154,7 @@ __device__ __forceinline__ void convert_x_items(int C, int base, const XItems &v
 // summed over the G lanes with DPP and, with S > 1, over the slices through
 // LDS in slice order.  All waves run the same number of rounds (batches past
 // the end read zeros), so the slice barriers are uniform.
-template <int CB, int U, int G>
+template <int CB, int U, int G, int GS>
 __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
                                                     const uint8_t *__restrict__ qs,
                                                     const uint32_t *__restrict__ sm,
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
     const int lane = threadIdx.x & 63, j = lane % G, rq = lane / G;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s = wave % S, bi = wave / S, B = (blockDim.x >> 6) / S;
-    const int C = K / 32, gpr = K / kGroup;
+    const int C = K / 32, gpr = K / GS;  // (scale, minimum) pairs per row
     const uint32_t rowbytes = K / 2;
     const int bstride = gridDim.x * B;
 
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
         const int n = min(b * RB + u * RPW + rq, N);
         const int c = j + G * ((s * P + pass) * CB + t);
         q[u][t] = buf_load16_nt(r_qs, (uint32_t)n * rowbytes + c * 16);
-        smv[u][t] = buf_load4_nt(r_sm, ((uint32_t)n * gpr + (c >> 3)) * 4u);
+        smv[u][t] = buf_load4_nt(r_sm, ((uint32_t)n * gpr + (GS == kGroup ? (c >> 3) : c)) * 4u);
     };
     XItems xv;
     load_x_items(r_x, C, 0, xv);
@@ -326,11 +326,11 @@ Dot2Cfg choose_dot2(int64_t N, int K, const DeviceInfo &dev)
     return c;
 }
 
-template <int CB, int U, int G>
+template <int CB, int U, int G, int GS>
 hipError_t run_dot2(Dot2Cfg c, const float *x, const uint8_t *qs, const uint16_t *sm, int64_t N,
                     int K, float *y, const DeviceInfo &dev, hipStream_t stream)
 {
-    const auto kernel = k_gemv_dot2<CB, U, G>;
+    const auto kernel = k_gemv_dot2<CB, U, G, GS>;
     if (c.rounds == 0) {
         // persistent: as many workgroups as fit on the chip at once, every wave
         // the same number of row batches (rounds) so no round runs half empty
@@ -353,26 +353,26 @@ hipError_t run_dot2(Dot2Cfg c, const float *x, const uint8_t *qs, const uint16_t
     return hipGetLastError();
 }
 
-template <int G>
+template <int G, int GS>
 hipError_t dispatch_dot2(const Dot2Cfg &c, const float *x, const uint8_t *qs, const uint16_t *sm,
                          int64_t N, int K, float *y, const DeviceInfo &dev, hipStream_t stream)
 {
     if (c.U == 1) {
         switch (c.CB) {
-        case 1: return run_dot2<1, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
-        case 2: return run_dot2<2, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
-        case 3: return run_dot2<3, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
-        case 4: return run_dot2<4, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
-        case 5: return run_dot2<5, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
-        case 6: return run_dot2<6, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
-        case 8: return run_dot2<8, 1, G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 1: return run_dot2<1, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 2: return run_dot2<2, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 3: return run_dot2<3, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 4: return run_dot2<4, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 5: return run_dot2<5, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 6: return run_dot2<6, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 8: return run_dot2<8, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
         }
     } else {
         switch (c.CB) {
-        case 1: return run_dot2<1, kRowStepsFor[1], G>(c, x, qs, sm, N, K, y, dev, stream);
-        case 2: return run_dot2<2, kRowStepsFor[2], G>(c, x, qs, sm, N, K, y, dev, stream);
-        case 3: return run_dot2<3, kRowStepsFor[3], G>(c, x, qs, sm, N, K, y, dev, stream);
-        case 4: return run_dot2<4, kRowStepsFor[4], G>(c, x, qs, sm, N, K, y, dev, stream);
+        case 1: return run_dot2<1, kRowStepsFor[1], G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 2: return run_dot2<2, kRowStepsFor[2], G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 3: return run_dot2<3, kRowStepsFor[3], G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 4: return run_dot2<4, kRowStepsFor[4], G, GS>(c, x, qs, sm, N, K, y, dev, stream);
         }
     }
     return hipErrorInvalidValue;
@@ -385,30 +385,43 @@ hipError_t dispatch_dot2(const Dot2Cfg &c, const float *x, const uint8_t *qs, co
 // rows >= M), so every weight byte fetched from HBM meets its activations
 // without another global read.  Weights are the B operand (16 weight rows x 32
 // k), so the lane that loads a weight row also loads that row's scale and
-// minimum and owns the row's outputs.
+// minimum and owns the row's outputs.  GS is the (scale, minimum) group along
+// K: 256, or 32 for the group-32 format, where each MFMA step is one run of 32
+// and carries its own pair.
 constexpr int kBRows = 16;                      // weight rows per unit (one MFMA column block)
 constexpr int kBWaves = 8;                      // waves per workgroup
 constexpr int kBThreads = kBWaves * kWave;
-constexpr int kBMaxGroups = 16;                 // K groups one workgroup holds in LDS
 constexpr int kBGroupLds = 8 * 4 * kBRows * 16; // A image of one group: [step 8][kg 4][m 16] x 16 B
-constexpr int kBFacLds = 3 * kBRows * 4;        // per group: f[16], X[16], c[16] (fp32)
 constexpr int kBDepth = 12;                     // (unit, group) items in flight per wave
 constexpr int kBTargetUnits = 256 * kBWaves;    // units wanted before K is split further
+constexpr int kBTileRow = 9 * 16;               // weight tile row: 8 chunks of 16 B + 16 B pad
 
-__host__ __device__ constexpr size_t arm_b_x_lds_bytes(int gps) { return (size_t)gps * (kBGroupLds + kBFacLds); }
-// activation image plus one weight transposition tile per wave (16 rows x 144 B)
-__host__ __device__ constexpr size_t arm_b_lds_bytes(int gps) { return arm_b_x_lds_bytes(gps) + kBWaves * 16 * 144; }
+// per group of 256: f[16] (and with GS 256: X[16], c[16]; with GS 32: X and c
+// per run, [8][16] each), fp32
+__host__ __device__ constexpr int arm_b_fac_floats(int GS) { return GS == 32 ? 16 + 2 * 8 * kBRows : 3 * kBRows; }
+// groups of 256 one workgroup holds in LDS
+__host__ __device__ constexpr int arm_b_max_groups(int GS) { return GS == 32 ? 14 : 16; }
+// per-wave tile: 16 weight rows x 144 B, and with GS 32 their 16 x 8 pairs
+__host__ __device__ constexpr int arm_b_tile_bytes(int GS) { return kBRows * kBTileRow + (GS == 32 ? kBRows * 8 * 4 : 0); }
+__host__ __device__ constexpr size_t arm_b_x_lds_bytes(int gps, int GS)
+{
+    return (size_t)gps * (kBGroupLds + 4 * arm_b_fac_floats(GS));
+}
+__host__ __device__ constexpr size_t arm_b_lds_bytes(int gps, int GS)
+{
+    return arm_b_x_lds_bytes(gps, GS) + (size_t)kBWaves * arm_b_tile_bytes(GS);
+}
 
 // Activations of groups g0 .. g0+gc-1 into LDS.  32 threads per (row m, group):
 // thread (c, t) converts dword t of chunk c, i.e. elements 32c+4t..32c+4t+3
 // (low nibbles) and 32c+16+4t..+3 (high nibbles, pre-scaled by 2^-4), in the
 // slot order the weight widening produces.  Per (group, row): the factor
 // f = 2^(24+e) that undoes the group's power-of-two scaling and the subnormal
-// weights, X = sum of x, and c = 7.5 * sum of (x - hi): the codes' mean share
-// of the fp16 rounding of x, folded back in exactly (the remaining error is
-// sum (x - hi) (q - 7.5), with centred codes).  Items are taken kXBatch per
-// thread at a time, all their loads issued before any is used; rows >= M and
-// items past the end read zeros (buffer bounds).
+// weights; per (group or run, row): X = sum of x and c = 7.5 * sum of (x - hi),
+// the codes' mean share of the fp16 rounding of x, folded back in exactly (the
+// remaining error is sum (x - hi) (q - 7.5), with centred codes).  Items are
+// taken kXBatch per thread at a time, all their loads issued before any is
+// used; rows >= M and items past the end read zeros (buffer bounds).
 constexpr int kXBatch = 8;
 
 struct XGroupItems {
@@ -432,9 +445,11 @@ __device__ __forceinline__ void load_x_groups(rsrc_t rx, int M, int K, int g0, i
     }
 }
 
+template <int GS>
 __device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupItems &v, uint8_t *lds)
 {
     float *fac = reinterpret_cast<float *>(lds + (size_t)gc * kBGroupLds);
+    constexpr int F = arm_b_fac_floats(GS);
 #pragma unroll
     for (int it = 0; it < kXBatch; ++it) {
         const int idx = base + threadIdx.x + it * blockDim.x;
@@ -445,11 +460,11 @@ __device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupI
         float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                            fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
         float sum = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+        // the power-of-two scale is per group of 256; the sums per (scale, minimum) group
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-            amax = fmaxf(amax, __shfl_xor(amax, o));
-            sum += __shfl_xor(sum, o);
-        }
+        for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+#pragma unroll
+        for (int o = 1; o < GS / 8; o <<= 1) sum += __shfl_xor(sum, o);
         const int sc = chunk_exp(amax);
         const float ls = ldexpf(1.0f, -sc), hs = ldexpf(1.0f, -sc - 4);
         // slot order of one widened dword: (4t, 4t+2) (16+4t, 16+4t+2) (4t+1, 4t+3) (16+4t+1, 16+4t+3)
@@ -465,15 +480,22 @@ __device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupI
         }
         float delta = ldexpf(dl, sc) + ldexpf(dh, sc + 4);
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) delta += __shfl_xor(delta, o);
+        for (int o = 1; o < GS / 8; o <<= 1) delta += __shfl_xor(delta, o);
         if (gl < gc) {
-            const int kg = c & 3, d = (c >> 2) * 4 + t;
+            // GS 256: step d mixes runs (kg = run & 3, d = (run >> 2) * 4 + dword);
+            // GS 32: step d is run d, lane kg its dword kg
+            const int kg = GS == 32 ? t : (c & 3), d = GS == 32 ? c : (c >> 2) * 4 + t;
             *reinterpret_cast<uint4 *>(lds + (size_t)gl * kBGroupLds + ((d * 4 + kg) * kBRows + m) * 16) =
                 make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            if (sub == 0) {
-                fac[(gl * 3 + 0) * kBRows + m] = ldexpf(1.0f, 24 + sc);
-                fac[(gl * 3 + 1) * kBRows + m] = sum;
-                fac[(gl * 3 + 2) * kBRows + m] = 7.5f * delta;
+            float *fg = fac + gl * F;
+            if (sub == 0) fg[m] = ldexpf(1.0f, 24 + sc);
+            if (GS == 32 && t == 0) {
+                fg[kBRows + c * kBRows + m] = sum;
+                fg[kBRows + 8 * kBRows + c * kBRows + m] = 7.5f * delta;
+            }
+            if (GS != 32 && sub == 0) {
+                fg[kBRows + m] = sum;
+                fg[2 * kBRows + m] = 7.5f * delta;
             }
         }
     }
@@ -487,27 +509,29 @@ __device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupI
 // soon as it is consumed, so D items of weights stay in flight with no
 // barrier in the loop.  The weights of an item (16 rows x 128 B) arrive as
 // whole 128-byte lines, 8 rows per load instruction, and are turned into the
-// MFMA B layout (lane (j, kg): row j, chunks kg and 4 + kg) through a small
-// per-wave LDS tile.  With kSmQuad (groups per split a multiple of 4) the
-// (scale, minimum) pairs come 4 groups per load, lane (j, kg) holding group
-// 4q + kg of row j, and reach the other lanes by a cross-lane read.  Items
-// past the wave's end load out of range (zeros) and write nothing.
-constexpr int kBTileRow = 9 * 16;                  // 8 chunks of 16 B + 16 B pad
-constexpr int kBTileLds = kBRows * kBTileRow;      // transposition tile per wave
-
-template <int D, bool kSmQuad>
+// MFMA B layout through a small per-wave LDS tile.  GS 256: lane (j, kg) takes
+// chunks kg and 4 + kg of row j; with kSmQuad (groups per split a multiple of
+// 4) the (scale, minimum) pairs come 4 groups per load, lane (j, kg) holding
+// group 4q + kg of row j, and reach the other lanes by a cross-lane read.
+// GS 32: step d is run d (lane (j, kg) its dword kg); the lane that loads a
+// run also loads the run's pair, which goes through the tile with the codes.
+// Items past the wave's end load out of range (zeros) and write nothing.
+template <int D, bool kSmQuad, int GS>
 __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict__ x,
                                                          const uint8_t *__restrict__ qs,
                                                          const uint32_t *__restrict__ sm,
                                                          float *__restrict__ out, int64_t ldo, int M,
                                                          int N, int K, int gps, int nsplit, int wps)
 {
-    static_assert(!kSmQuad || D % 4 == 0, "quads of slots");
+    static_assert(!kSmQuad || (D % 4 == 0 && GS == kGroup), "quads of slots, groups of 256");
+    constexpr bool kG32 = GS == 32;
+    constexpr int F = arm_b_fac_floats(GS);
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     const int lane = threadIdx.x & 63, j = lane & 15, kg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x % nsplit, wr = blockIdx.x / nsplit;
     const int GK = K / kGroup;
+    const int SPR = K / GS;  // (scale, minimum) pairs per row
     const int g0 = split * gps;
     const int gc = min(GK, g0 + gps) - g0;  // >= 1: the host makes every split non-empty
     const int R = (N + kBRows - 1) / kBRows;
@@ -516,12 +540,15 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
     const int nitems = nunits * gc;
     const uint32_t rowbytes = K / 2;
     float *dst = out + (int64_t)split * M * ldo;  // partials: [split][M][ldo]
-    uint8_t *tile = xl + arm_b_x_lds_bytes(gc) + wave * kBTileLds;
+    uint8_t *tile = xl + arm_b_x_lds_bytes(gc, GS) + wave * arm_b_tile_bytes(GS);
+    uint32_t *tile_sm = reinterpret_cast<uint32_t *>(tile + kBRows * kBTileRow);  // GS 32: [row][run]
 
     const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowbytes);
-    const rsrc_t r_sm = make_rsrc(sm, (uint32_t)N * GK * 4u);
-    uint4 wq[D][2];                     // rows 16 u + (lane >> 3) and + 8, chunk lane & 7
-    uint32_t wsm[kSmQuad ? D / 4 : D];  // (scale, minimum) pairs
+    const rsrc_t r_sm = make_rsrc(sm, (uint32_t)N * SPR * 4u);
+    uint4 wq[D][2];  // rows 16 u + (lane >> 3) and + 8, chunk lane & 7
+    // (scale, minimum) pairs: GS 256 per slot or per quad of slots; GS 32 the
+    // pairs of this lane's two rows and run
+    uint32_t wsm[kG32 ? 2 * D : (kSmQuad ? D / 4 : D)];
     auto load_item = [&](int s, int unit, int gl) {
         const bool ok = unit < nunits;
         const int r0 = (gw + GW * unit) * kBRows + (lane >> 3);
@@ -531,16 +558,20 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
         const uint32_t o1 = ok ? (uint32_t)min(r0 + 8, N) * rowbytes + gb : 0x80000000u;
         wq[s][0] = buf_load16_nt(r_qs, o0);
         wq[s][1] = buf_load16_nt(r_qs, o1);
-        if (!kSmQuad) {
+        if (kG32) {
+            const uint32_t run = (uint32_t)(g0 + gl) * 8u + (lane & 7);
+            wsm[2 * s] = buf_load4_nt(r_sm, ok ? ((uint32_t)min(r0, N) * SPR + run) * 4u : 0x80000000u);
+            wsm[2 * s + 1] = buf_load4_nt(r_sm, ok ? ((uint32_t)min(r0 + 8, N) * SPR + run) * 4u : 0x80000000u);
+        } else if (!kSmQuad) {
             const int n = min((gw + GW * unit) * kBRows + j, N);
-            wsm[s] = buf_load4_nt(r_sm, ok ? ((uint32_t)n * GK + g0 + gl) * 4u : 0x80000000u);
+            wsm[s] = buf_load4_nt(r_sm, ok ? ((uint32_t)n * SPR + g0 + gl) * 4u : 0x80000000u);
         }
     };
     // pairs of groups gl .. gl+3 of the unit: lane (j, kg) takes group gl + kg of row j
     auto load_quad = [&](int q, int unit, int gl) {
         const bool ok = unit < nunits;
         const int n = min((gw + GW * unit) * kBRows + j, N);
-        wsm[q] = buf_load4_nt(r_sm, ok ? ((uint32_t)n * GK + g0 + gl + kg) * 4u : 0x80000000u);
+        wsm[q] = buf_load4_nt(r_sm, ok ? ((uint32_t)n * SPR + g0 + gl + kg) * 4u : 0x80000000u);
     };
     // activation loads first, then the weight ring, then the conversion
     const rsrc_t r_x = make_rsrc(x, (uint32_t)M * K * 4u);
@@ -554,10 +585,10 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
         if (kSmQuad && s % 4 == 3) load_quad(s / 4, lu, lg - 3);
         if (++lg == gc) { lg = 0; ++lu; }
     }
-    convert_x_groups(gc, 0, xv, xl);
+    convert_x_groups<GS>(gc, 0, xv, xl);
     for (int base = kXBatch * kBThreads; base < nx; base += kXBatch * kBThreads) {
         load_x_groups(r_x, M, K, g0, gc, base, xv);
-        convert_x_groups(gc, base, xv, xl);
+        convert_x_groups<GS>(gc, base, xv, xl);
     }
     __syncthreads();
 
@@ -573,9 +604,20 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
             // weights of slot s through the tile: row r at r * kBTileRow, chunk c at 16 c
             *reinterpret_cast<uint4 *>(tile + (lane >> 3) * kBTileRow + (lane & 7) * 16) = wq[s][0];
             *reinterpret_cast<uint4 *>(tile + (8 + (lane >> 3)) * kBTileRow + (lane & 7) * 16) = wq[s][1];
-            const uint4 bw0 = *reinterpret_cast<const uint4 *>(tile + j * kBTileRow + kg * 16);
-            const uint4 bw1 = *reinterpret_cast<const uint4 *>(tile + j * kBTileRow + (4 + kg) * 16);
-            const uint32_t smv = kSmQuad ? (uint32_t)__shfl((int)wsm[s / 4], j + 16 * (s % 4)) : wsm[s];
+            uint4 bw0, bw1;
+            uint32_t smv = 0;
+            if (kG32) {
+                tile_sm[(lane >> 3) * 8 + (lane & 7)] = wsm[2 * s];
+                tile_sm[(8 + (lane >> 3)) * 8 + (lane & 7)] = wsm[2 * s + 1];
+                // dword kg of runs 0..7 of row j
+                const uint32_t *tr = reinterpret_cast<const uint32_t *>(tile + j * kBTileRow) + kg;
+                bw0 = make_uint4(tr[0], tr[4], tr[8], tr[12]);
+                bw1 = make_uint4(tr[16], tr[20], tr[24], tr[28]);
+            } else {
+                bw0 = *reinterpret_cast<const uint4 *>(tile + j * kBTileRow + kg * 16);
+                bw1 = *reinterpret_cast<const uint4 *>(tile + j * kBTileRow + (4 + kg) * 16);
+                smv = kSmQuad ? (uint32_t)__shfl((int)wsm[s / 4], j + 16 * (s % 4)) : wsm[s];
+            }
             // slot s is consumed: refill it in place with the item D later
             // (its (scale, minimum) quad once the last item using it is read)
             asm volatile("" : "+v"(yacc)::"memory");
@@ -584,27 +626,67 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
             if (++lg == gc) { lg = 0; ++lu; }
 
             const uint8_t *ag = xl + (size_t)cg * kBGroupLds + (kg * kBRows + j) * 16;
-            // two independent accumulator chains (even / odd steps)
-            float4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            const float *fg = fac + cg * F;
+            const float4 f = *reinterpret_cast<const float4 *>(fg + 4 * kg);
+            if (kG32) {
+                // one MFMA per run, each with its own (scale, minimum); two
+                // accumulators so a run's epilogue overlaps the next product
+                float4_t accs[2];
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                const half8_t a = *reinterpret_cast<const half8_t *>(ag + d * 4 * kBRows * 16);
-                const uint4 c4 = d < 4 ? bw0 : bw1;
-                const uint32_t w = (d & 3) == 0 ? c4.x : (d & 3) == 1 ? c4.y : (d & 3) == 2 ? c4.z : c4.w;
-                uint32_t p[4];
-                widen(w, p);
-                const half8_t b = __builtin_bit_cast(half8_t, uint4{p[0], p[1], p[2], p[3]});
-                acc2[d & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc2[d & 1], 0, 0, 0);
+                for (int d = 0; d < 8; ++d) {
+                    const half8_t a = *reinterpret_cast<const half8_t *>(ag + d * 4 * kBRows * 16);
+                    const uint4 c4 = d < 4 ? bw0 : bw1;
+                    const uint32_t w = (d & 3) == 0 ? c4.x : (d & 3) == 1 ? c4.y : (d & 3) == 2 ? c4.z : c4.w;
+                    uint32_t p[4];
+                    widen(w, p);
+                    const half8_t b = __builtin_bit_cast(half8_t, uint4{p[0], p[1], p[2], p[3]});
+                    accs[d & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    if (d > 0) {
+                        const int dp = d - 1;
+                        const float4_t acc = accs[dp & 1];
+                        const uint32_t sv = tile_sm[j * 8 + dp];
+                        const float sf = f16_bits_to_f32(sv & 0xFFFFu), mf = f16_bits_to_f32(sv >> 16);
+                        const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + dp * kBRows + 4 * kg);
+                        const float4 cc = *reinterpret_cast<const float4 *>(fg + 9 * kBRows + dp * kBRows + 4 * kg);
+                        yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
+                        yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
+                        yacc[2] = fmaf(sf, fmaf(f.z, acc[2], cc.z), fmaf(mf, X.z, yacc[2]));
+                        yacc[3] = fmaf(sf, fmaf(f.w, acc[3], cc.w), fmaf(mf, X.w, yacc[3]));
+                    }
+                }
+                {
+                    const float4_t acc = accs[1];
+                    const uint32_t sv = tile_sm[j * 8 + 7];
+                    const float sf = f16_bits_to_f32(sv & 0xFFFFu), mf = f16_bits_to_f32(sv >> 16);
+                    const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + 7 * kBRows + 4 * kg);
+                    const float4 cc = *reinterpret_cast<const float4 *>(fg + 9 * kBRows + 7 * kBRows + 4 * kg);
+                    yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
+                    yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
+                    yacc[2] = fmaf(sf, fmaf(f.z, acc[2], cc.z), fmaf(mf, X.z, yacc[2]));
+                    yacc[3] = fmaf(sf, fmaf(f.w, acc[3], cc.w), fmaf(mf, X.w, yacc[3]));
+                }
+            } else {
+                // two independent accumulator chains (even / odd steps)
+                float4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int d = 0; d < 8; ++d) {
+                    const half8_t a = *reinterpret_cast<const half8_t *>(ag + d * 4 * kBRows * 16);
+                    const uint4 c4 = d < 4 ? bw0 : bw1;
+                    const uint32_t w = (d & 3) == 0 ? c4.x : (d & 3) == 1 ? c4.y : (d & 3) == 2 ? c4.z : c4.w;
+                    uint32_t p[4];
+                    widen(w, p);
+                    const half8_t b = __builtin_bit_cast(half8_t, uint4{p[0], p[1], p[2], p[3]});
+                    acc2[d & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc2[d & 1], 0, 0, 0);
+                }
+                const float4_t acc = acc2[0] + acc2[1];
+                const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + 4 * kg);
+                const float4 cc = *reinterpret_cast<const float4 *>(fg + 2 * kBRows + 4 * kg);
+                const float sf = f16_bits_to_f32(smv & 0xFFFFu), mf = f16_bits_to_f32(smv >> 16);
+                yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
+                yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
+                yacc[2] = fmaf(sf, fmaf(f.z, acc[2], cc.z), fmaf(mf, X.z, yacc[2]));
+                yacc[3] = fmaf(sf, fmaf(f.w, acc[3], cc.w), fmaf(mf, X.w, yacc[3]));
             }
-            const float4_t acc = acc2[0] + acc2[1];
-            const float4 f = *reinterpret_cast<const float4 *>(fac + (cg * 3 + 0) * kBRows + 4 * kg);
-            const float4 X = *reinterpret_cast<const float4 *>(fac + (cg * 3 + 1) * kBRows + 4 * kg);
-            const float4 cc = *reinterpret_cast<const float4 *>(fac + (cg * 3 + 2) * kBRows + 4 * kg);
-            const float sf = f16_bits_to_f32(smv & 0xFFFFu), mf = f16_bits_to_f32(smv >> 16);
-            yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
-            yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
-            yacc[2] = fmaf(sf, fmaf(f.z, acc[2], cc.z), fmaf(mf, X.z, yacc[2]));
-            yacc[3] = fmaf(sf, fmaf(f.w, acc[3], cc.w), fmaf(mf, X.w, yacc[3]));
             if (cg == gc - 1) {
                 // unit complete: lane (j, kg) holds rows m = 4kg+e of column n
                 const int n = (gw + GW * cu) * kBRows + j;
@@ -645,62 +727,26 @@ struct MfmaCfg {
 // K split: as few splits as LDS allows, more while the 16-row units are too
 // few to give every wave of the chip one (small N), every split non-empty.
 // Independent of the device so the workspace size is too.
-MfmaCfg choose_mfma(int64_t N, int K)
+MfmaCfg choose_mfma(int64_t N, int K, int GS)
 {
     MfmaCfg c{};
     const int GK = K / kGroup;
     const int64_t R = (N + kBRows - 1) / kBRows;
-    int ns = (GK + kBMaxGroups - 1) / kBMaxGroups;
+    const int maxg = arm_b_max_groups(GS);
+    int ns = (GK + maxg - 1) / maxg;
     while (R * ns < kBTargetUnits && ns * 2 <= GK) ns *= 2;
     c.gps = (GK + ns - 1) / ns;
     c.nsplit = (GK + c.gps - 1) / c.gps;
     return c;
 }
 
-}  // namespace
-
-// Largest K whose activation image arm A holds in LDS (80 B per 32 of K plus
-// at most 2 KB of slice partials, within a workgroup's 160 KB); M = 1 calls
-// with a longer K take the matrix-core arm, which splits K over workgroups.
-constexpr int kArmAMaxK = 64512;
-
-size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
+template <int GS>
+hipError_t launch_arm_b(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                        int64_t ldy, int K, float *y, void *workspace, const DeviceInfo &dev,
+                        hipStream_t stream)
 {
-    if (M <= 1 && K <= kArmAMaxK) return 0;
-    const MfmaCfg c = choose_mfma(N, (int)K);
-    return c.nsplit > 1 ? (size_t)c.nsplit * M * N * sizeof(float) : 0;
-}
-
-static hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint16_t *sm,
-                                   int64_t N, int64_t ldy, int K, float *y, void *workspace,
-                                   const DeviceInfo &dev, hipStream_t stream);
-
-hipError_t launch_gemv(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
-                       int K, float *y, void *workspace, const DeviceInfo &dev, hipStream_t stream)
-{
-    // one descriptor addresses < 2 GiB of weights: split taller matrices into
-    // row ranges (y keeps its row stride N)
-    const int64_t rows_max = ((kMaxBufferBytes - 1) / (K / 2)) / 64 * 64;
-    for (int64_t n0 = 0; n0 < N; n0 += rows_max) {
-        const int64_t nn = N - n0 < rows_max ? N - n0 : rows_max;
-        const hipError_t e = launch_gemv_rows(x, M, qs + n0 * (K / 2), sm + n0 * (K / kGroup) * 2, nn,
-                                              N, K, y + n0, workspace, dev, stream);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-}
-
-static hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint16_t *sm,
-                                   int64_t N, int64_t ldy, int K, float *y, void *workspace,
-                                   const DeviceInfo &dev, hipStream_t stream)
-{
-    if (M == 1 && K <= kArmAMaxK) {
-        const Dot2Cfg c = choose_dot2(N, K, dev);
-        return c.G == 16 ? dispatch_dot2<16>(c, x, qs, sm, N, K, y, dev, stream)
-                         : dispatch_dot2<8>(c, x, qs, sm, N, K, y, dev, stream);
-    }
-    const MfmaCfg c = choose_mfma(N, K);
-    const size_t lds = arm_b_lds_bytes(c.gps);
+    const MfmaCfg c = choose_mfma(N, K, GS);
+    const size_t lds = arm_b_lds_bytes(c.gps, GS);
     if (lds > (size_t)dev.lds_bytes) return hipErrorInvalidConfiguration;
     const int64_t R = (N + kBRows - 1) / kBRows;
     // workgroups per split: one per CU overall, at most one per kBWaves units
@@ -710,16 +756,19 @@ static hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, con
     // split-K partials are dense [nsplit][M][N]; otherwise y is written directly
     float *out = c.nsplit > 1 ? static_cast<float *>(workspace) : y;
     const int64_t ldo = c.nsplit > 1 ? N : ldy;
-    // (scale, minimum) quads need every split's group count to be a multiple of 4
-    const bool quad = (K / kGroup) % c.gps == 0 && c.gps % 4 == 0;
-    if (quad)
-        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, true>), dim3((unsigned)(wps * c.nsplit)), dim3(kBThreads),
-                           lds, stream, x, qs, reinterpret_cast<const uint32_t *>(sm), out, ldo, M, (int)N,
-                           K, c.gps, c.nsplit, (int)wps);
-    else
-        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, false>), dim3((unsigned)(wps * c.nsplit)), dim3(kBThreads),
-                           lds, stream, x, qs, reinterpret_cast<const uint32_t *>(sm), out, ldo, M, (int)N,
-                           K, c.gps, c.nsplit, (int)wps);
+    const uint32_t *sm32 = reinterpret_cast<const uint32_t *>(sm);
+    const dim3 grid((unsigned)(wps * c.nsplit)), block(kBThreads);
+    if (GS == 32) {
+        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, false, 32>), grid, block, lds, stream, x, qs, sm32, out, ldo,
+                           M, (int)N, K, c.gps, c.nsplit, (int)wps);
+    } else if ((K / kGroup) % c.gps == 0 && c.gps % 4 == 0) {
+        // (scale, minimum) quads need every split's group count to be a multiple of 4
+        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, true, kGroup>), grid, block, lds, stream, x, qs, sm32, out,
+                           ldo, M, (int)N, K, c.gps, c.nsplit, (int)wps);
+    } else {
+        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, false, kGroup>), grid, block, lds, stream, x, qs, sm32, out,
+                           ldo, M, (int)N, K, c.gps, c.nsplit, (int)wps);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.nsplit == 1) return e;
     const int64_t count = (int64_t)M * N;
@@ -728,6 +777,61 @@ static hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, con
     hipLaunchKernelGGL(k_splitk_sum, dim3((unsigned)sb), dim3(256), 0, stream, out, y, M, (int)N, ldy,
                        c.nsplit);
     return hipGetLastError();
+}
+
+template <int GS>
+hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                            int64_t ldy, int K, float *y, void *workspace, const DeviceInfo &dev,
+                            hipStream_t stream);
+
+}  // namespace
+
+// Largest K whose activation image arm A holds in LDS (80 B per 32 of K plus
+// at most 2 KB of slice partials, within a workgroup's 160 KB); M = 1 calls
+// with a longer K take the matrix-core arm, which splits K over workgroups.
+constexpr int kArmAMaxK = 64512;
+
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group)
+{
+    if (M <= 1 && K <= kArmAMaxK) return 0;
+    const MfmaCfg c = choose_mfma(N, (int)K, group);
+    return c.nsplit > 1 ? (size_t)c.nsplit * M * N * sizeof(float) : 0;
+}
+
+namespace {
+
+template <int GS>
+hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                            int64_t ldy, int K, float *y, void *workspace, const DeviceInfo &dev,
+                            hipStream_t stream)
+{
+    if (M == 1 && K <= kArmAMaxK) {
+        const Dot2Cfg c = choose_dot2(N, K, dev);
+        return c.G == 16 ? dispatch_dot2<16, GS>(c, x, qs, sm, N, K, y, dev, stream)
+                         : dispatch_dot2<8, GS>(c, x, qs, sm, N, K, y, dev, stream);
+    }
+    return launch_arm_b<GS>(x, M, qs, sm, N, ldy, K, y, workspace, dev, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                       int K, int group, float *y, void *workspace, const DeviceInfo &dev,
+                       hipStream_t stream)
+{
+    // one descriptor addresses < 2 GiB of weights: split taller matrices into
+    // row ranges (y keeps its row stride N)
+    const int64_t rows_max = ((kMaxBufferBytes - 1) / (K / 2)) / 64 * 64;
+    for (int64_t n0 = 0; n0 < N; n0 += rows_max) {
+        const int64_t nn = N - n0 < rows_max ? N - n0 : rows_max;
+        const uint8_t *qs0 = qs + n0 * (K / 2);
+        const uint16_t *sm0 = sm + n0 * (K / group) * 2;
+        const hipError_t e =
+            group == 32 ? launch_gemv_rows<32>(x, M, qs0, sm0, nn, N, K, y + n0, workspace, dev, stream)
+                        : launch_gemv_rows<kGroup>(x, M, qs0, sm0, nn, N, K, y + n0, workspace, dev, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace q4mi

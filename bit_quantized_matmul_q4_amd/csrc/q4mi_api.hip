@@ -76,7 +76,8 @@ const char *q4_strerror(int code)
     }
 }
 
-int q4_pack(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm, void *stream)
+static int pack_common(const float *W, int64_t N, int64_t K, int group, uint8_t *qs, uint16_t *sm,
+                       void *stream)
 {
     if (N < 0 || N > Q4_MAX_N || !valid_k(K, 256)) return Q4_ERR_ARG;
     if (N == 0) return Q4_OK;
@@ -84,7 +85,17 @@ int q4_pack(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm, voi
     if (!aligned(W, 16) || !aligned(qs, 16) || !aligned(sm, 4)) return Q4_ERR_ALIGN;
     const DeviceInfo *dev = nullptr;
     if (int rc = current_device(&dev)) return rc;
-    return launch_status(q4mi::launch_q4_pack(W, N, K, qs, sm, dev->num_cus, (hipStream_t)stream));
+    return launch_status(q4mi::launch_q4_pack(W, N, K, group, qs, sm, dev->num_cus, (hipStream_t)stream));
+}
+
+int q4_pack(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm, void *stream)
+{
+    return pack_common(W, N, K, 256, qs, sm, stream);
+}
+
+int q4_pack_g32(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm, void *stream)
+{
+    return pack_common(W, N, K, 32, qs, sm, stream);
 }
 
 int q8_1_quantize(const float *x, int64_t M, int64_t K, int8_t *qa, uint16_t *ds, void *stream)
@@ -98,26 +109,41 @@ int q8_1_quantize(const float *x, int64_t M, int64_t K, int8_t *qa, uint16_t *ds
     return launch_status(q4mi::launch_q8_1_quantize(x, M, K, qa, ds, dev->num_cus, (hipStream_t)stream));
 }
 
-size_t q4_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
+static size_t gemv_ws_common(int64_t M, int64_t N, int64_t K, int group)
 {
     if (M < 0 || M > Q4_GEMV_MAX_M || N < 0 || N > Q4_MAX_N || !valid_k(K, 256)) return 0;
-    return q4mi::gemv_workspace_bytes(M, N, K);
+    return q4mi::gemv_workspace_bytes(M, N, K, group);
 }
 
-int q4_gemv(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N, int64_t K,
-            float *y, void *workspace, size_t ws_bytes, void *stream)
+size_t q4_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K) { return gemv_ws_common(M, N, K, 256); }
+size_t q4_gemv_g32_workspace_bytes(int64_t M, int64_t N, int64_t K) { return gemv_ws_common(M, N, K, 32); }
+
+static int gemv_common(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                       int64_t K, int group, float *y, void *workspace, size_t ws_bytes, void *stream)
 {
     if (M < 0 || M > Q4_GEMV_MAX_M || N < 0 || N > Q4_MAX_N || !valid_k(K, 256)) return Q4_ERR_ARG;
     if (M == 0 || N == 0) return Q4_OK;
     if (!x || !qs || !sm || !y) return Q4_ERR_ARG;
     if (!aligned(x, 16) || !aligned(qs, 16) || !aligned(sm, 4) || !aligned(y, 4)) return Q4_ERR_ALIGN;
-    const size_t need = q4mi::gemv_workspace_bytes(M, N, K);
+    const size_t need = q4mi::gemv_workspace_bytes(M, N, K, group);
     if (need > 0 && (!workspace || ws_bytes < need)) return Q4_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 16)) return Q4_ERR_ALIGN;
     const DeviceInfo *dev = nullptr;
     if (int rc = current_device(&dev)) return rc;
-    return launch_status(q4mi::launch_gemv(x, (int)M, qs, sm, N, (int)K, y, workspace, *dev,
+    return launch_status(q4mi::launch_gemv(x, (int)M, qs, sm, N, (int)K, group, y, workspace, *dev,
                                            (hipStream_t)stream));
+}
+
+int q4_gemv(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N, int64_t K,
+            float *y, void *workspace, size_t ws_bytes, void *stream)
+{
+    return gemv_common(x, M, qs, sm, N, K, 256, y, workspace, ws_bytes, stream);
+}
+
+int q4_gemv_g32(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N, int64_t K,
+                float *y, void *workspace, size_t ws_bytes, void *stream)
+{
+    return gemv_common(x, M, qs, sm, N, K, 32, y, workspace, ws_bytes, stream);
 }
 
 size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)

@@ -13,14 +13,16 @@ struct DeviceInfo {
     int lds_bytes;
 };
 
-hipError_t launch_q4_pack(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm,
+hipError_t launch_q4_pack(const float *W, int64_t N, int64_t K, int group, uint8_t *qs, uint16_t *sm,
                           int num_cus, hipStream_t stream);
 hipError_t launch_q8_1_quantize(const float *x, int64_t M, int64_t K, int8_t *qa, uint16_t *ds,
                                 int num_cus, hipStream_t stream);
 
-size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// group: the (scale, minimum) group along K, 256 or 32
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
 hipError_t launch_gemv(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
-                       int K, float *y, void *workspace, const DeviceInfo &dev, hipStream_t stream);
+                       int K, int group, float *y, void *workspace, const DeviceInfo &dev,
+                       hipStream_t stream);
 
 size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,

@@ -1,4 +1,4 @@
-// quantize.hip -- weight packing (4-bit, group 256, fp16 scale + minimum) and
+// quantize.hip -- weight packing (4-bit, groups of 256 or 32, fp16 scale + minimum) and
 // Q8_1 activation quantization for gfx950.
 //
 // Both kernels are HBM-streaming passes that must reproduce the defining fp32
@@ -15,14 +15,17 @@
 
 namespace q4mi {
 
-// One wave per group of 256 weights: lane l holds elements 4l .. 4l+3 (one
+// One wave per run of 256 weights: lane l holds elements 4l .. 4l+3 (one
 // 16-byte load per lane, 1 KiB per wave).  Codes of elements 32j+i and
 // 32j+i+16 share byte 16j+i, so the lane holding elements 32j+16+4u.. (lane%8
-// >= 4) hands its codes to lane-4, which writes one dword of four bytes.
+// >= 4) hands its codes to lane-4, which writes one dword of four bytes.  GS
+// is the (scale, minimum) group: 256 (the whole wave) or 32 (eight lanes).
+template <int GS>
 __global__ __launch_bounds__(256) void k_q4_pack(const float *__restrict__ W,
                                                  uint8_t *__restrict__ qs,
                                                  uint32_t *__restrict__ sm, int64_t ngroups)
 {
+    static_assert(GS == 256 || GS == 32, "group of 256 or 32");
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * (blockDim.x / kWave);
     for (int64_t grp = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
@@ -32,7 +35,7 @@ __global__ __launch_bounds__(256) void k_q4_pack(const float *__restrict__ W,
         float mn = fminf(fminf(v.x, v.y), fminf(v.z, v.w));
         float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
+        for (int o = GS / 8; o >= 1; o >>= 1) {
             mn = fminf(mn, __shfl_xor(mn, o));
             mx = fmaxf(mx, __shfl_xor(mx, o));
         }
@@ -58,7 +61,8 @@ __global__ __launch_bounds__(256) void k_q4_pack(const float *__restrict__ W,
             const int64_t byte = grp * (kGroup / 2) + 16 * (lane >> 3) + 4 * (lane & 7);
             *reinterpret_cast<uint32_t *>(qs + byte) = codes | (high << 4);
         }
-        if (lane == 0) sm[grp] = (uint32_t)s16 | ((uint32_t)m16 << 16);
+        if (GS == 256 && lane == 0) sm[grp] = (uint32_t)s16 | ((uint32_t)m16 << 16);
+        if (GS == 32 && (lane & 7) == 0) sm[grp * 8 + (lane >> 3)] = (uint32_t)s16 | ((uint32_t)m16 << 16);
     }
 }
 
@@ -95,15 +99,19 @@ __global__ __launch_bounds__(256) void k_q8_1_quantize(const float *__restrict__
     }
 }
 
-hipError_t launch_q4_pack(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm,
+hipError_t launch_q4_pack(const float *W, int64_t N, int64_t K, int group, uint8_t *qs, uint16_t *sm,
                           int num_cus, hipStream_t stream)
 {
-    const int64_t ngroups = N * (K / kGroup);
+    const int64_t ngroups = N * (K / kGroup);  // runs of 256 weights, one wave each
     int64_t blocks = (ngroups + 3) / 4;
     const int64_t cap = (int64_t)num_cus * 32;
     if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL(k_q4_pack, dim3((unsigned)blocks), dim3(256), 0, stream, W, qs,
-                       reinterpret_cast<uint32_t *>(sm), ngroups);
+    if (group == 32)
+        hipLaunchKernelGGL(k_q4_pack<32>, dim3((unsigned)blocks), dim3(256), 0, stream, W, qs,
+                           reinterpret_cast<uint32_t *>(sm), ngroups);
+    else
+        hipLaunchKernelGGL(k_q4_pack<256>, dim3((unsigned)blocks), dim3(256), 0, stream, W, qs,
+                           reinterpret_cast<uint32_t *>(sm), ngroups);
     return hipGetLastError();
 }
 

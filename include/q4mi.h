@@ -143,6 +143,23 @@ int q4_gemv(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, in
             int64_t K, float *y, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Group-32 variant (the "W4A16, asymmetric, group 32" int4 checkpoints the vLLM
+ * ROCM_OCTAVE pull request validates on, "Validation" and the QSA evaluation
+ * setup).  The code bytes qs are laid out exactly as for group 256; the
+ * (scale, minimum) pairs come one per 32 consecutive k: sm u16 [N][K/32][2].
+ * K must still be a positive multiple of 256.  Definitions, accuracy, argument
+ * rules and errors are those of the group-256 functions with "group of 256"
+ * read as "group of 32".
+ *   q4_pack_g32                  -- q4_pack over groups of 32.
+ *   q4_gemv_g32_workspace_bytes  -- workspace q4_gemv_g32 needs (host only).
+ *   q4_gemv_g32                  -- q4_gemv on group-32 weights.
+ */
+int q4_pack_g32(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm, void *stream);
+size_t q4_gemv_g32_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int q4_gemv_g32(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                int64_t K, float *y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * q4_mmq_workspace_bytes -- device workspace q4_mmq_gemm needs for this shape.
  * Pure host function.  Returns 0 for shapes q4_mmq_gemm would reject.
  */

@@ -19,3 +19,13 @@ def orc():
     o.build()
     o.set_mutation(0)
     return o
+
+
+@pytest.fixture(scope="session")
+def q4():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_matmul_q4_amd as m
+    m.lib()  # raises if the library is missing
+    return m

@@ -22,13 +22,6 @@ MAX_REL = 2e-3
 MAX_NMSE = 1e-6
 
 
-@pytest.fixture(scope="module")
-def q4():
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import bit_quantized_matmul_q4_amd as m
-    m.lib()  # raises if the library is missing
-    return m
 
 
 def say(*a):
