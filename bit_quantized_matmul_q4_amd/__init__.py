@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     q4_gemv_workspace_bytes,
     q4_mmq_block_dots,
     q4_mmq_gemm,
+    q4_mmq_gemm_g32,
     q4_mmq_gemm_q8_1,
     q4_mmq_workspace_bytes,
     q4_pack,

@@ -27,7 +27,7 @@ GEMV_MAX_M = 16
 SYMBOLS = [
     "q4_abi_version", "q4_strerror", "q4_pack", "q8_1_quantize", "q4_gemv_workspace_bytes",
     "q4_gemv", "q4_mmq_workspace_bytes", "q4_mmq_gemm", "q4_mmq_gemm_q8_1", "q4_mmq_block_dots",
-    "q4_pack_g32", "q4_gemv_g32_workspace_bytes", "q4_gemv_g32",
+    "q4_pack_g32", "q4_gemv_g32_workspace_bytes", "q4_gemv_g32", "q4_mmq_gemm_g32",
 ]
 
 _lib = None
@@ -63,6 +63,7 @@ def lib():
         "q4_pack_g32": ([P, I64, I64, P, P, P], I),
         "q4_gemv_g32_workspace_bytes": ([I64, I64, I64], SZ),
         "q4_gemv_g32": ([P, I64, P, P, I64, I64, P, P, SZ, P], I),
+        "q4_mmq_gemm_g32": ([P, P, I64, P, P, I64, I64, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -237,6 +238,23 @@ def q4_mmq_gemm_q8_1(qa, ds, qs, sm, qa_out=None, ds_out=None, workspace=None, s
     _check(lib().q4_mmq_gemm_q8_1(_ptr(qa), _ptr(ds), M, _ptr(qs), _ptr(sm), N, K, _ptr(qa_out),
                                   _ptr(ds_out), _ptr(ws), wsb, _stream(stream, qa)), "q4_mmq_gemm_q8_1")
     return qa_out, ds_out
+
+
+def q4_mmq_gemm_g32(qa, ds, qs, sm, y=None, workspace=None, stream=None):
+    """q4_mmq_gemm on group-32 weights (sm float16 [N][K/32][2])."""
+    M, K = qa.shape
+    N = qs.shape[0]
+    _need(qa, torch.int8, (M, K), "qa")
+    _need(ds, torch.float16, (M, K // 32, 2), "ds")
+    _need(qs, torch.uint8, (N, K // 2), "qs")
+    _need(sm, torch.float16, (N, K // 32, 2), "sm")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=qa.device)
+    _need(y, torch.float32, (M, N), "y")
+    ws, wsb = _workspace(q4_mmq_workspace_bytes(M, N, K), workspace, qa.device)
+    _check(lib().q4_mmq_gemm_g32(_ptr(qa), _ptr(ds), M, _ptr(qs), _ptr(sm), N, K, _ptr(y), _ptr(ws),
+                                 wsb, _stream(stream, qa)), "q4_mmq_gemm_g32")
+    return y
 
 
 def q4_mmq_block_dots(qa, qs, idot=None, stream=None):

@@ -50,7 +50,11 @@ constexpr int kLdsD = kTile * kBlocks * 4;   // d as fp32
 constexpr int kLdsX = kTile * 4;             // X[m][g] as fp32
 constexpr int kLdsSM = kTile * 8;            // (scale, minimum) as fp32 pairs
 constexpr int kLdsStage = kLdsA + kLdsB + kLdsD + kLdsX + kLdsSM;
-constexpr int kLdsTotal = kLdsStage;
+// Group-32 weights: the kLdsD region holds d16 | (sum a) << 16 per (block,
+// row) and the (scale, minimum) pairs are fp32 per (block, weight row):
+// 80 KiB, so two workgroups still share a CU.
+constexpr int kLdsSM32 = kTile * kBlocks * 8;
+__host__ __device__ constexpr int mmq_lds_bytes(bool g32) { return g32 ? kLdsA + kLdsB + kLdsD + kLdsSM32 : kLdsStage; }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -79,7 +83,9 @@ __device__ __forceinline__ int xcd_tile(int pid, int ntiles)
 // consumer that takes Q8_1 activations.
 enum { kOutY = 0, kOutDots = 1, kOutQ8 = 2 };
 
-template <int kMode>
+// kG32: group-32 weights, one (scale, minimum) pair per Q8_1 block, applied in
+// the per-block epilogue: y += scale * (d * I) + minimum * (d * sum a).
+template <int kMode, bool kG32 = false>
 __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
     const int8_t *__restrict__ qa, const uint32_t *__restrict__ ds, const uint8_t *__restrict__ qs,
     const uint32_t *__restrict__ sm, float *__restrict__ y, int32_t *__restrict__ idot,
@@ -87,12 +93,15 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
     int64_t ldi, int vec_store, int gps)
 {
     constexpr bool kDots = kMode == kOutDots;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTotal];
+    static_assert(!kG32 || kMode == kOutY, "group-32 weights: fp32 output");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[mmq_lds_bytes(kG32)];
     uint8_t *const sA = lds;
     uint8_t *const sB = lds + kLdsA;
     float *const sD = reinterpret_cast<float *>(lds + kLdsA + kLdsB);    // [block][row]
     float *const sX = reinterpret_cast<float *>(lds + kLdsA + kLdsB + kLdsD);
     float2 *const sSM = reinterpret_cast<float2 *>(lds + kLdsA + kLdsB + kLdsD + kLdsX);
+    uint32_t *const sDA = reinterpret_cast<uint32_t *>(lds + kLdsA + kLdsB);      // kG32: [block][row]
+    float2 *const sSM32 = reinterpret_cast<float2 *>(lds + kLdsA + kLdsB + kLdsD);  // kG32: [block][row]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
     const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowA);
     const rsrc_t r_qa = make_rsrc(qa, (uint32_t)M * (uint32_t)K);
     const rsrc_t r_ds = make_rsrc(ds, kDots ? 0u : (uint32_t)M * B * 4u);
-    const rsrc_t r_sm = make_rsrc(sm, kDots ? 0u : (uint32_t)N * G * 4u);
+    const rsrc_t r_sm = make_rsrc(sm, kDots ? 0u : (uint32_t)N * (kG32 ? B : G) * 4u);
 
     // ---- stage one group (256 of K) in LDS ----
     // weights: chunks tid and tid+512 (row idx/8, block idx%8), unpacked to int8;
@@ -120,7 +129,7 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
         const int arow = tid >> 2, aq = tid & 3;
         const int m = min(m0 + arow, M);  // rows past M or N read zeros
         uint4 w[2], a[4];
-        uint32_t dsw[2] = {0, 0}, psm = 0;
+        uint32_t dsw[2] = {0, 0}, psm = 0, psm32[2] = {0, 0};
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int idx = tid + 512 * p;
@@ -134,7 +143,16 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
             const uint32_t o = ((uint32_t)m * B + g * kBlocks + aq * 2) * 4u;
             dsw[0] = buf_load4(r_ds, o);
             dsw[1] = buf_load4(r_ds, o + 4);
-            if (tid < kTile) psm = buf_load4(r_sm, ((uint32_t)min(n0 + tid, N) * G + g) * 4u);
+            if (kG32) {
+                // pair of (weight row idx / 8, block idx % 8) for idx = tid, tid + 512
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int idx = tid + 512 * p;
+                    psm32[p] = buf_load4(r_sm, ((uint32_t)min(n0 + (idx >> 3), N) * B + g * kBlocks + (idx & 7)) * 4u);
+                }
+            } else if (tid < kTile) {
+                psm = buf_load4(r_sm, ((uint32_t)min(n0 + tid, N) * G + g) * 4u);
+            }
         }
         __syncthreads();  // every wave is done reading the previous group
 #pragma unroll
@@ -164,7 +182,10 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
                 sa = __builtin_amdgcn_sdot4((int)c1.z, 0x01010101, sa, false);
                 sa = __builtin_amdgcn_sdot4((int)c1.w, 0x01010101, sa, false);
                 const float d = f16_bits_to_f32(dsw[b2] & 0xFFFFu);
-                sD[(aq * 2 + b2) * kTile + arow] = d;  // block-major: conflict-free reads
+                if (kG32)  // |sum a| <= 4064 fits 16 bits
+                    sDA[(aq * 2 + b2) * kTile + arow] = (dsw[b2] & 0xFFFFu) | ((uint32_t)sa << 16);
+                else
+                    sD[(aq * 2 + b2) * kTile + arow] = d;  // block-major: conflict-free reads
                 xpart = fmaf(d, (float)sa, xpart);
             }
         }
@@ -172,9 +193,18 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
             // the row's eight blocks sit in four consecutive lanes
             xpart += __shfl_xor(xpart, 1);
             xpart += __shfl_xor(xpart, 2);
-            if (aq == 0) sX[arow] = xpart;
-            if (tid < kTile)
-                sSM[tid] = make_float2(f16_bits_to_f32(psm & 0xFFFFu), f16_bits_to_f32(psm >> 16));
+            if (kG32) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int idx = tid + 512 * p;
+                    sSM32[(idx & 7) * kTile + (idx >> 3)] =
+                        make_float2(f16_bits_to_f32(psm32[p] & 0xFFFFu), f16_bits_to_f32(psm32[p] >> 16));
+                }
+            } else {
+                if (aq == 0) sX[arow] = xpart;
+                if (tid < kTile)
+                    sSM[tid] = make_float2(f16_bits_to_f32(psm & 0xFFFFu), f16_bits_to_f32(psm >> 16));
+            }
         }
         __syncthreads();
     };
@@ -204,8 +234,30 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
         auto b_op = [&](int b) {
             return *reinterpret_cast<const v4i *>(sB + arow_w * kRow + b * 32 + half * 16);
         };
-        auto epilogue = [&](const v16i &I, int ta, float d, int b) {
-            if (kDots) {
+        // per block: d and (group-32 only) d * sum a of this lane's activation row
+        auto dscale = [&](int b) -> float2 {
+            if (kDots) return make_float2(0.0f, 0.0f);
+            if (kG32) {
+                const uint32_t v = sDA[b * kTile + arow_w];
+                const float d = f16_bits_to_f32(v & 0xFFFFu);
+                return make_float2(d, d * (float)(int)(int16_t)(v >> 16));  // exact: 11 x 12 bits
+            }
+            return make_float2(sD[b * kTile + arow_w], 0.0f);
+        };
+        auto epilogue = [&](const v16i &I, int ta, float2 dd, int b) {
+            const float d = dd.x;
+            if (kG32) {
+                // y += scale[n][b] * (d * I) + minimum[n][b] * (d * sum a); rows
+                // 8q + 4 half + r, two (scale, minimum) pairs per 16-byte read
+#pragma unroll
+                for (int p2 = 0; p2 < 8; ++p2) {
+                    const int e = 2 * p2;
+                    const float4 v = *reinterpret_cast<const float4 *>(
+                        sSM32 + b * kTile + wn * 64 + ta * 32 + 8 * (e >> 2) + 4 * half + (e & 3));
+                    yacc[ta][e] = fmaf(v.x, d * (float)I[e], fmaf(v.y, dd.y, yacc[ta][e]));
+                    yacc[ta][e + 1] = fmaf(v.z, d * (float)I[e + 1], fmaf(v.w, dd.y, yacc[ta][e + 1]));
+                }
+            } else if (kDots) {
                 const int m = m0 + arow_w;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -218,9 +270,9 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
             }
         };
         v4i a1 = a_op(0, 1), bv = b_op(0);
-        float dcur = kDots ? 0.0f : sD[arow_w];
+        float2 dcur = dscale(0);
         v16i prev = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op(0, 0), bv, zero, 0, 0, 0);
-        float dprev = dcur;
+        float2 dprev = dcur;
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) {
             // tile 1 of block b
@@ -235,7 +287,7 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
                              "+v"(gacc[1][15])::"memory");
                 bv = b_op(b + 1);
                 a1 = a_op(b + 1, 1);
-                dcur = kDots ? 0.0f : sD[(b + 1) * kTile + arow_w];
+                dcur = dscale(b + 1);
                 const v16i t0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_op(b + 1, 0), bv, zero, 0, 0, 0);
                 epilogue(prev, 1, dprev, b);
                 prev = t0;
@@ -244,7 +296,7 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
         }
         epilogue(prev, 1, dprev, kBlocks - 1);
 
-        if (!kDots) {
+        if (!kDots && !kG32) {
             // ---- group epilogue: weight scale and minimum ----
             // rows 8q + 4 half + r (r = 0..3) of each tile are consecutive:
             // two (scale, minimum) pairs per 16-byte read
@@ -403,10 +455,11 @@ SplitCfg choose_split(int64_t M, int64_t N, int K)
 // stay below 2 GiB, the reach of a buffer descriptor with 32-bit offsets.
 // With a K split, each sub-problem's partials go to the workspace (dense
 // [nsplit][mm][nn]) and a second kernel sums them into y (or into Q8_1).
-hipError_t run_tiles(int mode, const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+hipError_t run_tiles(int mode, bool g32, const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                      const uint16_t *sm, int64_t N, int K, float *y, int32_t *idot, int8_t *qo,
                      uint16_t *dso, void *workspace, int num_cus, hipStream_t stream)
 {
+    const int SPR = K / (g32 ? kBlock : kGroup);  // (scale, minimum) pairs per weight row
     const int64_t n_max = ((kMaxBufferBytes - 1) / (K / 2)) / kTile * kTile;
     const int64_t m_max = ((kMaxBufferBytes - 1) / K) / kTile * kTile;
     const int B = K / kBlock;
@@ -422,7 +475,7 @@ hipError_t run_tiles(int mode, const int8_t *qa, const uint16_t *ds, int64_t M, 
             const int8_t *qa0 = qa + m0 * K;
             const uint8_t *qs0 = qs + n0 * (K / 2);
             const uint32_t *ds0 = reinterpret_cast<const uint32_t *>(ds + m0 * B * 2);
-            const uint32_t *sm0 = reinterpret_cast<const uint32_t *>(sm + n0 * (K / kGroup) * 2);
+            const uint32_t *sm0 = reinterpret_cast<const uint32_t *>(sm + n0 * SPR * 2);
             if (mode == kOutDots) {
                 hipLaunchKernelGGL(k_mmq<kOutDots>, dim3((unsigned)tiles), dim3(512), 0, stream, qa0,
                                    (const uint32_t *)nullptr, qs0, (const uint32_t *)nullptr,
@@ -433,10 +486,16 @@ hipError_t run_tiles(int mode, const int8_t *qa, const uint16_t *ds, int64_t M, 
                 // partials [nsplit][mm][nn] in the workspace, then the sum
                 float *part = static_cast<float *>(workspace);
                 const int vec_store = (nn % 4 == 0) ? 1 : 0;
-                hipLaunchKernelGGL(k_mmq<kOutY>, dim3((unsigned)tiles, (unsigned)sc.nsplit), dim3(512), 0,
-                                   stream, qa0, ds0, qs0, sm0, part, (int32_t *)nullptr, (int8_t *)nullptr,
-                                   (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, nn, (int64_t)0,
-                                   vec_store, sc.gps);
+                if (g32)
+                    hipLaunchKernelGGL((k_mmq<kOutY, true>), dim3((unsigned)tiles, (unsigned)sc.nsplit), dim3(512),
+                                       0, stream, qa0, ds0, qs0, sm0, part, (int32_t *)nullptr, (int8_t *)nullptr,
+                                       (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, nn, (int64_t)0,
+                                       vec_store, sc.gps);
+                else
+                    hipLaunchKernelGGL(k_mmq<kOutY>, dim3((unsigned)tiles, (unsigned)sc.nsplit), dim3(512), 0,
+                                       stream, qa0, ds0, qs0, sm0, part, (int32_t *)nullptr, (int8_t *)nullptr,
+                                       (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, nn, (int64_t)0,
+                                       vec_store, sc.gps);
                 if (hipGetLastError() == hipSuccess) {
                     int64_t sb = (mm * nn + 255) / 256;
                     if (sb > (int64_t)num_cus * 8) sb = (int64_t)num_cus * 8;
@@ -452,9 +511,14 @@ hipError_t run_tiles(int mode, const int8_t *qa, const uint16_t *ds, int64_t M, 
                 float *y0 = y + m0 * N + n0;
                 const int vec_store = (N % 4 == 0) && (nn % 4 == 0) &&
                                       ((reinterpret_cast<uintptr_t>(y0) & 15) == 0);
-                hipLaunchKernelGGL(k_mmq<kOutY>, dim3((unsigned)tiles, 1u), dim3(512), 0, stream, qa0, ds0, qs0,
-                                   sm0, y0, (int32_t *)nullptr, (int8_t *)nullptr, (uint32_t *)nullptr,
-                                   (int)mm, (int)nn, K, tiles_m, N, (int64_t)0, vec_store, sc.gps);
+                if (g32)
+                    hipLaunchKernelGGL((k_mmq<kOutY, true>), dim3((unsigned)tiles, 1u), dim3(512), 0, stream, qa0,
+                                       ds0, qs0, sm0, y0, (int32_t *)nullptr, (int8_t *)nullptr, (uint32_t *)nullptr,
+                                       (int)mm, (int)nn, K, tiles_m, N, (int64_t)0, vec_store, sc.gps);
+                else
+                    hipLaunchKernelGGL(k_mmq<kOutY>, dim3((unsigned)tiles, 1u), dim3(512), 0, stream, qa0, ds0,
+                                       qs0, sm0, y0, (int32_t *)nullptr, (int8_t *)nullptr, (uint32_t *)nullptr,
+                                       (int)mm, (int)nn, K, tiles_m, N, (int64_t)0, vec_store, sc.gps);
             } else {
                 hipLaunchKernelGGL(k_mmq<kOutQ8>, dim3((unsigned)tiles, 1u), dim3(512), 0, stream, qa0, ds0,
                                    qs0, sm0, (float *)nullptr, (int32_t *)nullptr, qo + m0 * N + n0,
@@ -486,23 +550,31 @@ hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uin
                       const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
                       const DeviceInfo &dev, hipStream_t stream)
 {
-    return run_tiles(kOutY, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace, dev.num_cus,
-                     stream);
+    return run_tiles(kOutY, false, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
+                     dev.num_cus, stream);
+}
+
+hipError_t launch_mmq_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                          const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
+                          const DeviceInfo &dev, hipStream_t stream)
+{
+    return run_tiles(kOutY, true, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
+                     dev.num_cus, stream);
 }
 
 hipError_t launch_mmq_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                            const uint16_t *sm, int64_t N, int K, int8_t *qo, uint16_t *dso,
                            void *workspace, const DeviceInfo &dev, hipStream_t stream)
 {
-    return run_tiles(kOutQ8, qa, ds, M, qs, sm, N, K, nullptr, nullptr, qo, dso, workspace, dev.num_cus,
-                     stream);
+    return run_tiles(kOutQ8, false, qa, ds, M, qs, sm, N, K, nullptr, nullptr, qo, dso, workspace,
+                     dev.num_cus, stream);
 }
 
 hipError_t launch_block_dots(const int8_t *qa, int64_t M, const uint8_t *qs, int64_t N, int K,
                              int32_t *idot, const DeviceInfo &dev, hipStream_t stream)
 {
-    return run_tiles(kOutDots, qa, nullptr, M, qs, nullptr, N, K, nullptr, idot, nullptr, nullptr, nullptr,
-                     dev.num_cus, stream);
+    return run_tiles(kOutDots, false, qa, nullptr, M, qs, nullptr, N, K, nullptr, idot, nullptr, nullptr,
+                     nullptr, dev.num_cus, stream);
 }
 
 }  // namespace q4mi

@@ -152,9 +152,9 @@ size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)
     return q4mi::mmq_workspace_bytes(M, N, K);
 }
 
-int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
-                const uint16_t *sm, int64_t N, int64_t K, float *y, void *workspace,
-                size_t ws_bytes, void *stream)
+static int mmq_common(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                      const uint16_t *sm, int64_t N, int64_t K, bool g32, float *y, void *workspace,
+                      size_t ws_bytes, void *stream)
 {
     if (M < 0 || M > Q4_MAX_M_MMQ || N < 0 || N > Q4_MAX_N || !valid_k(K, 256)) return Q4_ERR_ARG;
     if (M == 0 || N == 0) return Q4_OK;
@@ -166,8 +166,24 @@ int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *
     if (need > 0 && !aligned(workspace, 16)) return Q4_ERR_ALIGN;
     const DeviceInfo *dev = nullptr;
     if (int rc = current_device(&dev)) return rc;
-    return launch_status(q4mi::launch_mmq(qa, ds, M, qs, sm, N, (int)K, y, workspace, *dev,
-                                          (hipStream_t)stream));
+    return launch_status(g32 ? q4mi::launch_mmq_g32(qa, ds, M, qs, sm, N, (int)K, y, workspace, *dev,
+                                                    (hipStream_t)stream)
+                             : q4mi::launch_mmq(qa, ds, M, qs, sm, N, (int)K, y, workspace, *dev,
+                                                (hipStream_t)stream));
+}
+
+int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                const uint16_t *sm, int64_t N, int64_t K, float *y, void *workspace,
+                size_t ws_bytes, void *stream)
+{
+    return mmq_common(qa, ds, M, qs, sm, N, K, false, y, workspace, ws_bytes, stream);
+}
+
+int q4_mmq_gemm_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                    const uint16_t *sm, int64_t N, int64_t K, float *y, void *workspace,
+                    size_t ws_bytes, void *stream)
+{
+    return mmq_common(qa, ds, M, qs, sm, N, K, true, y, workspace, ws_bytes, stream);
 }
 
 int q4_mmq_gemm_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,

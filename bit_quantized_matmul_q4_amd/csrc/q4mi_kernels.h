@@ -28,6 +28,9 @@ size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                       const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
                       const DeviceInfo &dev, hipStream_t stream);
+hipError_t launch_mmq_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                          const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
+                          const DeviceInfo &dev, hipStream_t stream);
 hipError_t launch_mmq_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                            const uint16_t *sm, int64_t N, int K, int8_t *qo, uint16_t *dso,
                            void *workspace, const DeviceInfo &dev, hipStream_t stream);

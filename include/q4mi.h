@@ -153,11 +153,20 @@ int q4_gemv(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, in
  *   q4_pack_g32                  -- q4_pack over groups of 32.
  *   q4_gemv_g32_workspace_bytes  -- workspace q4_gemv_g32 needs (host only).
  *   q4_gemv_g32                  -- q4_gemv on group-32 weights.
+ *   q4_mmq_gemm_g32              -- q4_mmq_gemm on group-32 weights; each Q8_1
+ *                                   block meets its own weight pair, so the
+ *                                   scales apply per block:
+ *       y[m][n] = sum_b ( scale[n][b] * d[m][b] * I[m][n][b]
+ *                         + minimum[n][b] * d[m][b] * sum_{k in b} a[m][k] )
+ *     (workspace: q4_mmq_workspace_bytes(M, N, K)).
  */
 int q4_pack_g32(const float *W, int64_t N, int64_t K, uint8_t *qs, uint16_t *sm, void *stream);
 size_t q4_gemv_g32_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int q4_gemv_g32(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N,
                 int64_t K, float *y, void *workspace, size_t ws_bytes, void *stream);
+int q4_mmq_gemm_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                    const uint16_t *sm, int64_t N, int64_t K, float *y, void *workspace,
+                    size_t ws_bytes, void *stream);
 
 /*
  * q4_mmq_workspace_bytes -- device workspace q4_mmq_gemm needs for this shape.

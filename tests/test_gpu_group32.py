@@ -108,3 +108,53 @@ def test_gemv_g32_equal_pairs_match_g256(q4, orc):
     y32 = q4.q4_gemv_g32(dev(x), qs, sm32).cpu().numpy()
     y256 = q4.q4_gemv(dev(x), qs, sm).cpu().numpy()
     close(y32, y256, "g32 repeated vs g256")
+
+
+def mmq_g32_check(q4, orc, M, N, K, seed, outliers, what, mrows=None):
+    W, x = wl.mmq_case(seed, M, N, K, outliers)
+    qs, sm = q4.q4_pack_g32(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    y = q4.q4_mmq_gemm_g32(qa, ds, qs, sm)
+    torch.cuda.synchronize()
+    qs_h = qs.cpu().numpy()
+    sm_h = sm.cpu().view(torch.int16).numpy().view(np.uint16)
+    qa_h = qa.cpu().numpy()
+    ds_h = ds.cpu().view(torch.int16).numpy().view(np.uint16)
+    yh = y.cpu().numpy()
+    sel = slice(None) if mrows is None else mrows
+    ref = orc.q4_mmq(qa_h[sel], ds_h[sel], qs_h, sm_h, K, group=G32)
+    close(yh[sel], ref, what)
+
+
+@pytest.mark.parametrize("M,N,K,outl", [(1, 1, 256, False), (130, 129, 768, True),
+                                        (128, 128, 2560, False), (257, 385, 1024, True),
+                                        (100, 200, 2048, True), (64, 1000, 4096, False)])
+def test_mmq_g32_parity(q4, orc, M, N, K, outl):
+    say("mmq g32 M=%d N=%d K=%d outliers=%s" % (M, N, K, outl))
+    mmq_g32_check(q4, orc, M, N, K, M + N + 3, outl, "mmq g32 %dx%dx%d" % (M, N, K))
+
+
+def test_mmq_g32_512(q4, orc):
+    c = wl.MMQ_512
+    say("mmq g32 M=512 K=2560 N=9216 (sampled activation rows)")
+    rows = np.unique(np.concatenate([[0, 511], np.random.default_rng(5).choice(512, 62, replace=False)]))
+    mmq_g32_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq g32 512", mrows=rows)
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_mmq_g32_2048(q4, orc, idx):
+    c = wl.MMQ_2048[idx]
+    say("mmq g32 M=2048 %s (sampled activation rows)" % c["name"])
+    rows = np.unique(np.concatenate([[0, 2047], np.random.default_rng(9 + idx).choice(2048, 30, replace=False)]))
+    mmq_g32_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq g32 2048 " + c["name"],
+                  mrows=rows)
+
+
+def test_mmq_g32_equal_pairs_match_g256(q4, orc):
+    say("mmq g32 with repeated pairs vs g256")
+    W, x = wl.mmq_case(12, 300, 700, 2560, True)
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    sm32 = sm.repeat_interleave(8, dim=1).contiguous()
+    close(q4.q4_mmq_gemm_g32(qa, ds, qs, sm32).cpu().numpy(), q4.q4_mmq_gemm(qa, ds, qs, sm).cpu().numpy(),
+          "mmq g32 repeated vs g256")
