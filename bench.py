@@ -343,6 +343,53 @@ def prefill_sweep(q4, wl, dev, stream):
     return out
 
 
+def group32_figures(q4, wl, dev, stream):
+    """The group-32 variant on the same shapes: lm_head GEMV at M = 1 and 8
+    (two weight copies in turn), and the M = 2048 gate/up MMQ.  Bytes count the
+    group-32 pairs: N*K/2 + N*K/32*4."""
+    import torch
+
+    def timed(fn, reps=6):
+        fn()
+        ts = []
+        for r in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn(r)
+            b.record(stream)
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return sorted(x.elapsed_time(y) for x, y in ts)[len(ts) // 2] * 1e3
+
+    out = {}
+    _, K, N = wl.DECODE_PROJECTIONS[7]
+    copies = []
+    for i in range(2):
+        W = wl.draw_weights(wl.generator(7 + 100 * i, dev), N, K, dev)
+        copies.append(q4.q4_pack_g32(W))
+        del W
+    for M in (1, 8):
+        x = wl.draw_activations(wl.generator(M, dev), M, K, False, dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = torch.empty((max(1, q4.q4_gemv_g32_workspace_bytes(M, N, K)),), dtype=torch.uint8, device=dev)
+        us = timed(lambda r=0: q4.q4_gemv_g32(x, *copies[r % 2], y=y, workspace=ws))
+        nbytes = N * K // 2 + N * (K // 32) * 4 + M * K * 4 + M * N * 4
+        out["gemv_lm_head_M%d" % M] = {"us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                       "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del copies
+    c = wl.MMQ_2048[0]
+    W, x = wl.mmq_case(c["seed"], c["M"], c["N"], c["K"], c["outliers"], dev)
+    qs, sm = q4.q4_pack_g32(W)
+    del W
+    qa, ds = q4.q8_1_quantize(x)
+    y = torch.empty((c["M"], c["N"]), dtype=torch.float32, device=dev)
+    us = timed(lambda r=0: q4.q4_mmq_gemm_g32(qa, ds, qs, sm, y=y))
+    ops = 2.0 * c["M"] * c["N"] * c["K"]
+    out["mmq_M2048_gate_up"] = {"us": round(us, 1), "tops": round(ops / (us * 1e-6) / 1e12, 1),
+                                "frac_i8_peak": round(ops / (us * 1e-6) / 1e12 / I8_PEAK_TOPS, 4)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -562,6 +609,7 @@ def main():
         out["gemv_tiny_m"] = tiny_m_sweep(q4, wl, dev, stream)
     if not args.no_prefill_sweep:
         out["prefill_sweep"] = prefill_sweep(q4, wl, dev, stream)
+    out["group32"] = group32_figures(q4, wl, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
