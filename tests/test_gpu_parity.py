@@ -375,3 +375,42 @@ def test_mmq_deterministic(q4, orc):
     a = q4.q4_mmq_gemm(qa, ds, qs, sm)
     b = q4.q4_mmq_gemm(qa, ds, qs, sm)
     assert torch.equal(a, b)
+
+
+def _mmq_vs_oracle(q4, orc, W, x, what):
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    y = q4.q4_mmq_gemm(qa, ds, qs, sm).cpu().numpy()
+    ref = orc.q4_mmq(qa.cpu().numpy(), ds.cpu().view(torch.int16).numpy().view(np.uint16), qs.cpu().numpy(),
+                     sm.cpu().view(torch.int16).numpy().view(np.uint16), W.shape[1])
+    close(y, ref, what)
+
+
+def test_mmq_extreme_block_sums(q4, orc):
+    # The fp32-output MMQ sums each group's eight block dots in int32 with
+    # 13-bit block scales.  Near its bound: every activation at +-127 with all
+    # block scales equal (D = 8191) against groups whose 255 lowest weights
+    # give code 0 (centred -8), i.e. |block dot| close to 32 * 127 * 8.
+    say("mmq near the int32 bound of the group sums")
+    M, N, K = 130, 100, 2048
+    rng = np.random.default_rng(11)
+    W = torch.full((N, K), -0.01, dtype=torch.float32)
+    W[:, 255::256] = 0.03  # one maximum per group: scale != 0, all other codes 0
+    W[N // 2:] = torch.from_numpy((0.02 * rng.standard_normal((N - N // 2, K))).astype(np.float32))
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32))
+    x[0:40] = 1.5
+    x[40:80] = -2.5
+    _mmq_vs_oracle(q4, orc, W, x, "mmq extreme block sums")
+
+
+def test_mmq_massive_activations(q4, orc):
+    # block scales within one group far apart: one channel 1000x, 1 % of the
+    # rest 100x
+    say("mmq with a 1000x channel and 100x outliers")
+    M, N, K = 257, 385, 1024
+    rng = np.random.default_rng(12)
+    W = torch.from_numpy((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x = np.where(rng.random((M, K)) < 0.01, x * 100, x).astype(np.float32)
+    x[:, 7] *= 1000
+    _mmq_vs_oracle(q4, orc, W, torch.from_numpy(x), "mmq massive activations")
