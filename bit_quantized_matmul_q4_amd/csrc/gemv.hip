@@ -85,19 +85,29 @@ constexpr int kChunkLds = 80;
 // activation items per thread whose loads go out ahead of the weight loads
 constexpr int kFillRegs = 2;
 
-// Item idx = (chunk c, dword i) of the image needs x[32c+4i..+3] (low nibbles)
-// and x[32c+16+4i..+3] (high nibbles).  Thread t takes items base + t + it *
-// blockDim.x; items past the end read zeros and are not stored.
+// Item idx = (row r, chunk c, dword i), idx = (r C + c) 4 + i, of the image
+// needs x[r][32c+4i..+3] (low nibbles) and x[r][32c+16+4i..+3] (high
+// nibbles); the image holds the rows one after another, so item idx belongs
+// to chunk idx / 4 of it.  Thread t takes items base + t + it * blockDim.x;
+// items past the end (nitems) read zeros and are not stored, rows >= M read
+// zeros.
 struct XItems {
     float4 a[kFillRegs], b[kFillRegs];
 };
 
-__device__ __forceinline__ void load_x_items(rsrc_t rx, int C, int base, XItems &v)
+template <int MR>
+__device__ __forceinline__ void load_x_items(rsrc_t rx, int C, int K, int M, int nitems, int base, XItems &v)
 {
 #pragma unroll
     for (int it = 0; it < kFillRegs; ++it) {
         const int idx = base + threadIdx.x + it * blockDim.x;
-        const uint32_t off = idx < C * 4 ? (uint32_t)((idx >> 2) * 32 + 4 * (idx & 3)) * 4u : 0x80000000u;
+        uint32_t off;
+        if (MR == 1) {
+            off = idx < nitems ? (uint32_t)((idx >> 2) * 32 + 4 * (idx & 3)) * 4u : 0x80000000u;
+        } else {
+            const int r = idx / (C * 4), e = idx - r * (C * 4);
+            off = idx < nitems && r < M ? (uint32_t)(r * K + (e >> 2) * 32 + 4 * (e & 3)) * 4u : 0x80000000u;
+        }
         v.a[it] = __builtin_bit_cast(float4, buf_load16(rx, off));
         v.b[it] = __builtin_bit_cast(float4, buf_load16(rx, off + 64));
     }
@@ -105,7 +115,7 @@ __device__ __forceinline__ void load_x_items(rsrc_t rx, int C, int base, XItems 
 
 // Four consecutive threads hold the four dwords of one chunk (blockDim is a
 // multiple of 64, so they are active together).
-__device__ __forceinline__ void convert_x_items(int C, int base, const XItems &v, uint8_t *lds)
+__device__ __forceinline__ void convert_x_items(int nitems, int base, const XItems &v, uint8_t *lds)
 {
 #pragma unroll
     for (int it = 0; it < kFillRegs; ++it) {
@@ -134,7 +144,7 @@ __device__ __forceinline__ void convert_x_items(int C, int base, const XItems &v
         float delta = ldexpf(dl, sc) + ldexpf(dh, sc + 4);
         delta += __shfl_xor(delta, 1);
         delta += __shfl_xor(delta, 2);
-        if (idx < C * 4) {
+        if (idx < nitems) {
             uint8_t *dst = lds + (idx >> 2) * kChunkLds;
             const int i = idx & 3;
             *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
@@ -153,13 +163,15 @@ __device__ __forceinline__ void convert_x_items(int C, int base, const XItems &v
 // the fp16 image is built while the weights are in flight.  Row partials are
 // summed over the G lanes with DPP and, with S > 1, over the slices through
 // LDS in slice order.  All waves run the same number of rounds (batches past
-// the end read zeros), so the slice barriers are uniform.
-template <int CB, int U, int G, int GS>
+// the end read zeros), so the slice barriers are uniform.  MR activation rows
+// (1 or 2; rows >= M are zeros and not written) share every widened weight
+// pair: the image holds one copy per row, y row r starts at y + r * ldy.
+template <int CB, int U, int G, int GS, int MR>
 __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
                                                     const uint8_t *__restrict__ qs,
                                                     const uint32_t *__restrict__ sm,
-                                                    float *__restrict__ y, int N, int K, int S, int P,
-                                                    int rounds)
+                                                    float *__restrict__ y, int64_t ldy, int M, int N,
+                                                    int K, int S, int P, int rounds)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
     constexpr int RPW = kWave / G;
@@ -168,12 +180,13 @@ __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s = wave % S, bi = wave / S, B = (blockDim.x >> 6) / S;
     const int C = K / 32, gpr = K / GS;  // (scale, minimum) pairs per row
+    const int nx = MR * C * 4;           // activation image items
     const uint32_t rowbytes = K / 2;
     const int bstride = gridDim.x * B;
 
     const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowbytes);
     const rsrc_t r_sm = make_rsrc(sm, (uint32_t)N * gpr * 4u);
-    const rsrc_t r_x = make_rsrc(x, (uint32_t)K * 4u);
+    const rsrc_t r_x = make_rsrc(x, (uint32_t)M * K * 4u);
     uint4 q[U][CB];
     uint32_t smv[U][CB];
     // rows past the end (every row of a batch past the last) read zeros
@@ -184,45 +197,62 @@ __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
         smv[u][t] = buf_load4_nt(r_sm, ((uint32_t)n * gpr + (GS == kGroup ? (c >> 3) : c)) * 4u);
     };
     XItems xv;
-    load_x_items(r_x, C, 0, xv);
+    load_x_items<MR>(r_x, C, K, M, nx, 0, xv);
     int b = blockIdx.x * B + bi;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int t = 0; t < CB; ++t) load_item(b, 0, u, t);
-    convert_x_items(C, 0, xv, xl);
-    for (int base = kFillRegs * blockDim.x; base < C * 4; base += kFillRegs * blockDim.x) {
-        load_x_items(r_x, C, base, xv);
-        convert_x_items(C, base, xv, xl);
+    convert_x_items(nx, 0, xv, xl);
+    for (int base = kFillRegs * blockDim.x; base < nx; base += kFillRegs * blockDim.x) {
+        load_x_items<MR>(r_x, C, K, M, nx, base, xv);
+        convert_x_items(nx, base, xv, xl);
     }
     __syncthreads();
-    float *red = reinterpret_cast<float *>(xl + C * kChunkLds);  // [B][S][RB] slice partials
+    float *red = reinterpret_cast<float *>(xl + MR * C * kChunkLds);  // [B][S][RB][MR] slice partials
 
-    float p[U];
+    float p[U][MR];
 #pragma unroll
-    for (int u = 0; u < U; ++u) p[u] = 0.0f;
-    for (int r = 0; r < rounds; ++r) {
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < MR; ++r) p[u][r] = 0.0f;
+    auto fence = [&]() {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < MR; ++r) asm volatile("" : "+v"(p[u][r])::"memory");
+    };
+    for (int rd = 0; rd < rounds; ++rd) {
         const int nb = b + bstride;  // past the end in the last round: zeros
         for (int pass = 0; pass < P; ++pass) {
             const int lb = pass + 1 < P ? b : nb, lp = pass + 1 < P ? pass + 1 : 0;
 #pragma unroll
             for (int t = 0; t < CB; ++t) {
                 // The partial sums of chunk t-1 must exist before chunk t's
-                // activation reads are issued: only one chunk's 16 activation
+                // activation reads are issued: only one chunk's activation
                 // registers are live, and the loads refilled below stay in flight.
-#pragma unroll
-                for (int u = 0; u < U; ++u) asm volatile("" : "+v"(p[u])::"memory");
+                fence();
                 const int c = j + G * ((s * P + pass) * CB + t);
-                const uint8_t *xc = xl + c * kChunkLds;
-                uint4 hv[4];
+                uint32_t xh[MR][16];
+                float4 fx[MR];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) hv[i] = *reinterpret_cast<const uint4 *>(xc + 16 * i);
-                const float4 fx = *reinterpret_cast<const float4 *>(xc + 64);
-                const uint32_t xh[16] = {hv[0].x, hv[0].y, hv[0].z, hv[0].w, hv[1].x, hv[1].y, hv[1].z, hv[1].w,
-                                         hv[2].x, hv[2].y, hv[2].z, hv[2].w, hv[3].x, hv[3].y, hv[3].z, hv[3].w};
+                for (int r = 0; r < MR; ++r) {
+                    const uint8_t *xc = xl + (r * C + c) * kChunkLds;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint4 hv = *reinterpret_cast<const uint4 *>(xc + 16 * i);
+                        xh[r][4 * i] = hv.x;
+                        xh[r][4 * i + 1] = hv.y;
+                        xh[r][4 * i + 2] = hv.z;
+                        xh[r][4 * i + 3] = hv.w;
+                    }
+                    fx[r] = *reinterpret_cast<const float4 *>(xc + 64);
+                }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    float acc = 0.0f;
+                    float acc[MR];
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) acc[r] = 0.0f;
                     const uint32_t w4[4] = {q[u][t].x, q[u][t].y, q[u][t].z, q[u][t].w};
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
@@ -230,42 +260,50 @@ __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
                         widen(w4[d], pw);
 #pragma unroll
                         for (int k = 0; k < 4; ++k)
-                            acc = __builtin_amdgcn_fdot2(as_half2(pw[k]), as_half2(xh[4 * d + k]), acc, false);
+#pragma unroll
+                            for (int r = 0; r < MR; ++r)
+                                acc[r] = __builtin_amdgcn_fdot2(as_half2(pw[k]), as_half2(xh[r][4 * d + k]), acc[r],
+                                                                false);
                     }
                     const uint32_t sv = smv[u][t];
                     const float sf = f16_bits_to_f32(sv & 0xFFFFu), mf = f16_bits_to_f32(sv >> 16);
-                    p[u] = fmaf(sf, fmaf(fx.x, acc, fx.z), fmaf(mf, fx.y, p[u]));
+#pragma unroll
+                    for (int r = 0; r < MR; ++r)
+                        p[u][r] = fmaf(sf, fmaf(fx[r].x, acc[r], fx[r].z), fmaf(mf, fx[r].y, p[u][r]));
                 }
                 // registers of chunk t are consumed: refill them in place (the
                 // fence keeps the loads below the compute, so the loaded
                 // registers are the loop-carried ones and need no copy)
-#pragma unroll
-                for (int u = 0; u < U; ++u) asm volatile("" : "+v"(p[u])::"memory");
+                fence();
 #pragma unroll
                 for (int u = 0; u < U; ++u) load_item(lb, lp, u, t);
             }
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float v = group_sum<G>(p[u]);
-            p[u] = 0.0f;
-            const int n = b * RB + u * RPW + rq;
-            if (S == 1) {
-                if (j == 0 && n < N) y[n] = v;
-            } else if (j == 0) {
-                red[(bi * S + s) * RB + u * RPW + rq] = v;
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const float v = group_sum<G>(p[u][r]);
+                p[u][r] = 0.0f;
+                const int n = b * RB + u * RPW + rq;
+                if (S == 1) {
+                    if (j == 0 && n < N && r < M) y[r * ldy + n] = v;
+                } else if (j == 0) {
+                    red[((bi * S + s) * RB + u * RPW + rq) * MR + r] = v;
+                }
             }
-        }
         if (S > 1) {
             __syncthreads();
             if (s == 0 && j == 0) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    float v = 0.0f;
-                    for (int k = 0; k < S; ++k) v += red[(bi * S + k) * RB + u * RPW + rq];
-                    const int n = b * RB + u * RPW + rq;
-                    if (n < N) y[n] = v;
-                }
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) {
+                        float v = 0.0f;
+                        for (int k = 0; k < S; ++k) v += red[((bi * S + k) * RB + u * RPW + rq) * MR + r];
+                        const int n = b * RB + u * RPW + rq;
+                        if (n < N && r < M) y[r * ldy + n] = v;
+                    }
             }
             __syncthreads();
         }
@@ -288,7 +326,8 @@ struct Dot2Cfg {
 // workgroup, which amortises the activation image over 4 S waves, or one
 // batch per workgroup when that leaves fewer workgroups than half the CUs.
 // Large N: persistent waves (S = 1), every wave the same number of batches.
-Dot2Cfg choose_dot2(int64_t N, int K, const DeviceInfo &dev)
+// MR activation rows only change the LDS the image takes.
+Dot2Cfg choose_dot2(int64_t N, int K, int MR, const DeviceInfo &dev)
 {
     Dot2Cfg c{};
     const int C = K / 32;
@@ -329,15 +368,15 @@ Dot2Cfg choose_dot2(int64_t N, int K, const DeviceInfo &dev)
         }
         c.rounds = 0;  // set at launch from the kernel's occupancy
     }
-    c.lds = (size_t)C * kChunkLds + (size_t)c.B * c.S * rpw * c.U * sizeof(float);
+    c.lds = (size_t)MR * C * kChunkLds + (size_t)c.B * c.S * rpw * c.U * MR * sizeof(float);
     return c;
 }
 
-template <int CB, int U, int G, int GS>
-hipError_t run_dot2(Dot2Cfg c, const float *x, const uint8_t *qs, const uint16_t *sm, int64_t N,
-                    int K, float *y, const DeviceInfo &dev, hipStream_t stream)
+template <int CB, int U, int G, int GS, int MR>
+hipError_t run_dot2(Dot2Cfg c, const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                    int64_t ldy, int K, float *y, const DeviceInfo &dev, hipStream_t stream)
 {
-    const auto kernel = k_gemv_dot2<CB, U, G, GS>;
+    const auto kernel = k_gemv_dot2<CB, U, G, GS, MR>;
     if (c.rounds == 0) {
         // persistent: as many workgroups as fit on the chip at once, every wave
         // the same number of row batches (rounds) so no round runs half empty
@@ -356,31 +395,31 @@ hipError_t run_dot2(Dot2Cfg c, const float *x, const uint8_t *qs, const uint16_t
         c.grid = (int)((waves + c.B - 1) / c.B);
     }
     hipLaunchKernelGGL(kernel, dim3(c.grid), dim3(kWave * c.B * c.S), c.lds, stream, x, qs,
-                       reinterpret_cast<const uint32_t *>(sm), y, (int)N, K, c.S, c.P, c.rounds);
+                       reinterpret_cast<const uint32_t *>(sm), y, ldy, M, (int)N, K, c.S, c.P, c.rounds);
     return hipGetLastError();
 }
 
-template <int G, int GS>
-hipError_t dispatch_dot2(const Dot2Cfg &c, const float *x, const uint8_t *qs, const uint16_t *sm,
-                         int64_t N, int K, float *y, const DeviceInfo &dev, hipStream_t stream)
+template <int G, int GS, int MR>
+hipError_t dispatch_dot2(const Dot2Cfg &c, const float *x, int M, const uint8_t *qs, const uint16_t *sm,
+                         int64_t N, int64_t ldy, int K, float *y, const DeviceInfo &dev, hipStream_t stream)
 {
-    if (c.CB == 5 && c.U == 2) return run_dot2<5, 2, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+    if (c.CB == 5 && c.U == 2) return run_dot2<5, 2, G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
     if (c.U == 1) {
         switch (c.CB) {
-        case 1: return run_dot2<1, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
-        case 2: return run_dot2<2, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
-        case 3: return run_dot2<3, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
-        case 4: return run_dot2<4, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
-        case 5: return run_dot2<5, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
-        case 6: return run_dot2<6, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
-        case 8: return run_dot2<8, 1, G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 1: return run_dot2<1, 1, G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 2: return run_dot2<2, 1, G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 3: return run_dot2<3, 1, G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 4: return run_dot2<4, 1, G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 5: return run_dot2<5, 1, G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 6: return run_dot2<6, 1, G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 8: return run_dot2<8, 1, G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
         }
     } else {
         switch (c.CB) {
-        case 1: return run_dot2<1, kRowStepsFor[1], G, GS>(c, x, qs, sm, N, K, y, dev, stream);
-        case 2: return run_dot2<2, kRowStepsFor[2], G, GS>(c, x, qs, sm, N, K, y, dev, stream);
-        case 3: return run_dot2<3, kRowStepsFor[3], G, GS>(c, x, qs, sm, N, K, y, dev, stream);
-        case 4: return run_dot2<4, kRowStepsFor[4], G, GS>(c, x, qs, sm, N, K, y, dev, stream);
+        case 1: return run_dot2<1, kRowStepsFor[1], G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 2: return run_dot2<2, kRowStepsFor[2], G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 3: return run_dot2<3, kRowStepsFor[3], G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 4: return run_dot2<4, kRowStepsFor[4], G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
         }
     }
     return hipErrorInvalidValue;
@@ -794,14 +833,18 @@ hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint
 
 }  // namespace
 
-// Largest K whose activation image arm A holds in LDS (80 B per 32 of K plus
-// at most 2 KB of slice partials, within a workgroup's 160 KB); M = 1 calls
-// with a longer K take the matrix-core arm, which splits K over workgroups.
+// Largest K whose activation image arm A holds in LDS (80 B per 32 of K and
+// activation row plus at most 2 KB of slice partials per row, within a
+// workgroup's 160 KB), for one and for two rows; longer K takes the
+// matrix-core arm, which splits K over workgroups.
 constexpr int kArmAMaxK = 64512;
+constexpr int kArmAMaxK2 = 31744;
+
+bool arm_a_takes(int64_t M, int64_t K) { return (M == 1 && K <= kArmAMaxK) || (M == 2 && K <= kArmAMaxK2); }
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group)
 {
-    if (M <= 1 && K <= kArmAMaxK) return 0;
+    if (M < 1 || arm_a_takes(M, K)) return 0;
     const MfmaCfg c = choose_mfma(N, (int)K, group);
     return c.nsplit > 1 ? (size_t)c.nsplit * M * N * sizeof(float) : 0;
 }
@@ -813,10 +856,13 @@ hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint
                             int64_t ldy, int K, float *y, void *workspace, const DeviceInfo &dev,
                             hipStream_t stream)
 {
-    if (M == 1 && K <= kArmAMaxK) {
-        const Dot2Cfg c = choose_dot2(N, K, dev);
-        return c.G == 16 ? dispatch_dot2<16, GS>(c, x, qs, sm, N, K, y, dev, stream)
-                         : dispatch_dot2<8, GS>(c, x, qs, sm, N, K, y, dev, stream);
+    if (arm_a_takes(M, K)) {
+        const Dot2Cfg c = choose_dot2(N, K, M, dev);
+        if (M == 1)
+            return c.G == 16 ? dispatch_dot2<16, GS, 1>(c, x, 1, qs, sm, N, ldy, K, y, dev, stream)
+                             : dispatch_dot2<8, GS, 1>(c, x, 1, qs, sm, N, ldy, K, y, dev, stream);
+        return c.G == 16 ? dispatch_dot2<16, GS, 2>(c, x, 2, qs, sm, N, ldy, K, y, dev, stream)
+                         : dispatch_dot2<8, GS, 2>(c, x, 2, qs, sm, N, ldy, K, y, dev, stream);
     }
     return launch_arm_b<GS>(x, M, qs, sm, N, ldy, K, y, workspace, dev, stream);
 }

@@ -234,6 +234,28 @@ def test_gemv_rows_match_single_row_calls(q4, orc):
         close(y1.cpu().numpy()[0], y[m].cpu().numpy(), "row %d" % m)
 
 
+def test_gemv_two_rows_match_single_row_calls(q4, orc):
+    # M = 2 runs the one-row arm with both rows sharing every widened weight:
+    # each row's arithmetic is a one-row call's, so the results are identical
+    # (small N in one round, the lm_head width persistent, K at the largest
+    # two-row image and just beyond it, where the matrix-core arm takes over)
+    for N, K, seed in [(700, 2560, 21), (37984, 4096, 22), (300, 31744, 23), (96, 32000, 24)]:
+        say("gemv M=2 vs one-row calls N=%d K=%d" % (N, K))
+        W, x = wl.gemv_case(seed, 2, N, K)
+        qs, sm = q4.q4_pack(dev(W))
+        xd = dev(x)
+        y = q4.q4_gemv(xd, qs, sm)
+        for m in range(2):
+            y1 = q4.q4_gemv(xd[m:m + 1].contiguous(), qs, sm)
+            if K <= 31744:
+                assert torch.equal(y1[0], y[m]), "row %d" % m
+            else:
+                close(y1.cpu().numpy()[0], y[m].cpu().numpy(), "row %d" % m)
+        if N <= 700:
+            ref = orc.q4_gemv(x.numpy(), qs.cpu().numpy(), sm.cpu().view(torch.int16).numpy().view(np.uint16), K)
+            close(y.cpu().numpy(), ref, "gemv M=2 %dx%d" % (N, K))
+
+
 def test_gemv_one_hot_and_deterministic(q4, orc):
     say("gemv one-hot x and rerun determinism")
     N, K = 333, 2560
