@@ -314,6 +314,9 @@ __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
 // row steps U per chunk-block size CB in the persistent mode: about 8-10 loads
 // of 16 B in flight per lane
 constexpr int kRowStepsFor[9] = {0, 8, 4, 2, 2, 1, 1, 1, 1};
+// with four activation rows (64 activation registers) fewer row steps fit
+constexpr int kRowStepsFor4[9] = {0, 4, 2, 2, 2, 1, 1, 1, 1};
+__host__ __device__ constexpr int row_steps(int CB, int MR) { return MR == 4 ? kRowStepsFor4[CB] : kRowStepsFor[CB]; }
 
 struct Dot2Cfg {
     int G, CB, U, S, P, B, rounds, grid;
@@ -355,7 +358,7 @@ Dot2Cfg choose_dot2(int64_t N, int K, int MR, const DeviceInfo &dev)
         c.rounds = 1;
         c.grid = (int)((nb1 + c.B - 1) / c.B);
     } else {
-        c.U = kRowStepsFor[c.CB];
+        c.U = row_steps(c.CB, MR);
         c.S = 1;
         c.P = cpt / c.CB;
         c.B = 4;
@@ -416,10 +419,10 @@ hipError_t dispatch_dot2(const Dot2Cfg &c, const float *x, int M, const uint8_t 
         }
     } else {
         switch (c.CB) {
-        case 1: return run_dot2<1, kRowStepsFor[1], G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
-        case 2: return run_dot2<2, kRowStepsFor[2], G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
-        case 3: return run_dot2<3, kRowStepsFor[3], G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
-        case 4: return run_dot2<4, kRowStepsFor[4], G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 1: return run_dot2<1, row_steps(1, MR), G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 2: return run_dot2<2, row_steps(2, MR), G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 3: return run_dot2<3, row_steps(3, MR), G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        case 4: return run_dot2<4, row_steps(4, MR), G, GS, MR>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
         }
     }
     return hipErrorInvalidValue;
@@ -839,12 +842,27 @@ hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint
 // matrix-core arm, which splits K over workgroups.
 constexpr int kArmAMaxK = 64512;
 constexpr int kArmAMaxK2 = 31744;
+constexpr int kArmAMaxK4 = 15360;
 
-bool arm_a_takes(int64_t M, int64_t K) { return (M == 1 && K <= kArmAMaxK) || (M == 2 && K <= kArmAMaxK2); }
+// Activation rows arm A's image holds for an M-row call (0: the matrix-core
+// arm).  One and two rows always (measured faster at every N); three and four
+// rows only below 65536 weight rows: there the matrix-core arm's fixed costs
+// (activation image per workgroup, K split with a second pass) dominate
+// (4096 x 4096 at M = 4: 9.8 vs 20.6 us), while on the lm_head widths four
+// rows make arm A VALU-bound (88 vs 72 us at K = 4096).  A function of the
+// shape only, so the workspace query agrees with the launch.
+constexpr int64_t kArmA4MaxN = 65536;
+int arm_a_rows(int64_t M, int64_t N, int64_t K)
+{
+    if (M == 1 && K <= kArmAMaxK) return 1;
+    if (M == 2 && K <= kArmAMaxK2) return 2;
+    if (M >= 3 && M <= 4 && K <= kArmAMaxK4 && N < kArmA4MaxN) return 4;
+    return 0;
+}
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group)
 {
-    if (M < 1 || arm_a_takes(M, K)) return 0;
+    if (M < 1 || arm_a_rows(M, N, K) != 0) return 0;
     const MfmaCfg c = choose_mfma(N, (int)K, group);
     return c.nsplit > 1 ? (size_t)c.nsplit * M * N * sizeof(float) : 0;
 }
@@ -856,13 +874,17 @@ hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint
                             int64_t ldy, int K, float *y, void *workspace, const DeviceInfo &dev,
                             hipStream_t stream)
 {
-    if (arm_a_takes(M, K)) {
-        const Dot2Cfg c = choose_dot2(N, K, M, dev);
-        if (M == 1)
-            return c.G == 16 ? dispatch_dot2<16, GS, 1>(c, x, 1, qs, sm, N, ldy, K, y, dev, stream)
-                             : dispatch_dot2<8, GS, 1>(c, x, 1, qs, sm, N, ldy, K, y, dev, stream);
-        return c.G == 16 ? dispatch_dot2<16, GS, 2>(c, x, 2, qs, sm, N, ldy, K, y, dev, stream)
-                         : dispatch_dot2<8, GS, 2>(c, x, 2, qs, sm, N, ldy, K, y, dev, stream);
+    const int MR = arm_a_rows(M, N, K);
+    if (MR != 0) {
+        const Dot2Cfg c = choose_dot2(N, K, MR, dev);
+        if (MR == 1)
+            return c.G == 16 ? dispatch_dot2<16, GS, 1>(c, x, M, qs, sm, N, ldy, K, y, dev, stream)
+                             : dispatch_dot2<8, GS, 1>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        if (MR == 2)
+            return c.G == 16 ? dispatch_dot2<16, GS, 2>(c, x, M, qs, sm, N, ldy, K, y, dev, stream)
+                             : dispatch_dot2<8, GS, 2>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
+        return c.G == 16 ? dispatch_dot2<16, GS, 4>(c, x, M, qs, sm, N, ldy, K, y, dev, stream)
+                         : dispatch_dot2<8, GS, 4>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
     }
     return launch_arm_b<GS>(x, M, qs, sm, N, ldy, K, y, workspace, dev, stream);
 }

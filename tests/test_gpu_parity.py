@@ -234,26 +234,32 @@ def test_gemv_rows_match_single_row_calls(q4, orc):
         close(y1.cpu().numpy()[0], y[m].cpu().numpy(), "row %d" % m)
 
 
-def test_gemv_two_rows_match_single_row_calls(q4, orc):
-    # M = 2 runs the one-row arm with both rows sharing every widened weight:
-    # each row's arithmetic is a one-row call's, so the results are identical
-    # (small N in one round, the lm_head width persistent, K at the largest
-    # two-row image and just beyond it, where the matrix-core arm takes over)
-    for N, K, seed in [(700, 2560, 21), (37984, 4096, 22), (300, 31744, 23), (96, 32000, 24)]:
-        say("gemv M=2 vs one-row calls N=%d K=%d" % (N, K))
-        W, x = wl.gemv_case(seed, 2, N, K)
-        qs, sm = q4.q4_pack(dev(W))
-        xd = dev(x)
-        y = q4.q4_gemv(xd, qs, sm)
-        for m in range(2):
-            y1 = q4.q4_gemv(xd[m:m + 1].contiguous(), qs, sm)
-            if K <= 31744:
-                assert torch.equal(y1[0], y[m]), "row %d" % m
-            else:
-                close(y1.cpu().numpy()[0], y[m].cpu().numpy(), "row %d" % m)
-        if N <= 700:
-            ref = orc.q4_gemv(x.numpy(), qs.cpu().numpy(), sm.cpu().view(torch.int16).numpy().view(np.uint16), K)
-            close(y.cpu().numpy(), ref, "gemv M=2 %dx%d" % (N, K))
+# (M, N, K, seed, VALU arm): up to 4 rows run the one-row arm when the image
+# fits (K <= 31744 for 2 rows, 15360 for 4) and, for 3-4 rows, N < 65536
+FEW_ROW_CASES = [(2, 700, 2560, 21, True), (2, 37984, 4096, 22, True), (2, 300, 31744, 23, True),
+                 (2, 96, 32000, 24, False), (3, 700, 2560, 25, True), (4, 1000, 15360, 26, True),
+                 (4, 300, 15616, 27, False), (4, 65535, 2560, 28, True), (4, 65536, 2560, 29, False)]
+
+
+@pytest.mark.parametrize("M,N,K,seed,valu", FEW_ROW_CASES)
+def test_gemv_few_rows_match_single_row_calls(q4, orc, M, N, K, seed, valu):
+    # On the VALU arm the rows share every widened weight pair and each row's
+    # arithmetic is a one-row call's, so the results are identical; on the
+    # matrix-core arm they agree to the fp32 tolerance.
+    say("gemv M=%d vs one-row calls N=%d K=%d" % (M, N, K))
+    W, x = wl.gemv_case(seed, M, N, K)
+    qs, sm = q4.q4_pack(dev(W))
+    xd = dev(x)
+    y = q4.q4_gemv(xd, qs, sm)
+    for m in range(M):
+        y1 = q4.q4_gemv(xd[m:m + 1].contiguous(), qs, sm)
+        if valu:
+            assert torch.equal(y1[0], y[m]), "row %d" % m
+        else:
+            close(y1.cpu().numpy()[0], y[m].cpu().numpy(), "row %d" % m)
+    if N <= 1000:
+        ref = orc.q4_gemv(x.numpy(), qs.cpu().numpy(), sm.cpu().view(torch.int16).numpy().view(np.uint16), K)
+        close(y.cpu().numpy(), ref, "gemv M=%d %dx%d" % (M, N, K))
 
 
 def test_gemv_one_hot_and_deterministic(q4, orc):
