@@ -117,6 +117,23 @@ def test_q8_1_bitexact(q4, orc, M, K, outl):
     assert np.array_equal(ds_g.cpu().view(torch.int16).numpy().view(np.uint16), ds_o)
 
 
+def test_q8_1_beyond_one_descriptor(q4, orc):
+    # 8200 x 65536 activations (2.15 GB of fp32) take two launches, the first
+    # covering 536870880 elements (just under 2 GiB), so the boundary falls
+    # inside row 8191; rows around it and the last row are checked bit for bit
+    M, K = 8200, 65536
+    say("q8_1 M=%d K=%d (two launches)" % (M, K))
+    g = torch.Generator(device="cuda").manual_seed(31)
+    x = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32)
+    qa_g, ds_g = q4.q8_1_quantize(x)
+    torch.cuda.synchronize()
+    for r0, r1 in ((0, 1), (8190, 8193), (M - 1, M)):
+        qa_o, ds_o = orc.q8_1_quantize(x[r0:r1].cpu().numpy())
+        assert np.array_equal(qa_g[r0:r1].cpu().numpy(), qa_o), (r0, r1)
+        assert np.array_equal(ds_g[r0:r1].cpu().view(torch.int16).numpy().view(np.uint16), ds_o), (r0, r1)
+    del x, qa_g, ds_g
+
+
 def test_q8_1_edge_values(q4, orc):
     say("q8_1 edge values")
     rng = np.random.default_rng(22)
