@@ -328,11 +328,12 @@ struct Dot2Cfg {
     size_t lds;
 };
 
-// Two modes.  Small N (up to about 12 row batches per CU): one round in which
-// every wave makes a single pass, CB the largest chunk block dividing the
-// lane's chunks and K split over S = chunks / CB waves; four batches per
-// workgroup, which amortises the activation image over 4 S waves, or one
-// batch per workgroup when that leaves fewer workgroups than half the CUs.
+// Two modes.  Small N (up to about 12 row batches per CU): one round, CB the
+// largest chunk block dividing the lane's chunks (for rows of 12 or more
+// chunk steps at most a sixth of them), K split over S waves of P passes;
+// four batches per workgroup, which amortises the activation image over 4 S
+// waves, or one batch per workgroup when that leaves fewer workgroups than an
+// eighth of the CUs.
 // Large N: persistent waves (S = 1), every wave the same number of batches.
 // MR activation rows only change the LDS the image takes.
 Dot2Cfg choose_dot2(int64_t N, int K, int MR, const DeviceInfo &dev)
@@ -350,7 +351,15 @@ Dot2Cfg choose_dot2(int64_t N, int K, int MR, const DeviceInfo &dev)
     if (nb1 <= (int64_t)dev.num_cus * 12) {
         c.U = 1;
         c.B = 4;
-        if ((nb1 + c.B - 1) / c.B < dev.num_cus / 2) {
+        if (cpt >= 12) {
+            // long rows: at least 6 chunk steps per row, so each of the (up
+            // to 4) slices makes two passes and refills while it computes
+            // (9216 -> 2560: 6.4 -> 5.7 us)
+            for (int cb : cbs)
+                if (cpt % cb == 0 && cb * 6 <= cpt) { c.CB = cb; break; }
+        }
+        if ((nb1 + c.B - 1) / c.B < dev.num_cus / 8) {
+            // very few rows: one batch per workgroup, K over more slices
             c.B = 1;
             c.CB = 1;
         }
