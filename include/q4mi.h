@@ -179,10 +179,15 @@ size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * note: pre-quantized Q8_1 activations, LDS-staged tiles, integer matrix-core
  * products over 128x128 output tiles):
  *     y[m][n] = sum_k (d[m][k/32] * a[m][k]) * (scale[n][k/256] * q[n][k] + minimum[n][k/256])
- * Per-block products sum_{k in block} a * q are exact int32 (i8 MFMA); block
- * and group scales are applied in fp32.  Results match the fp64 definition to
- * max|dy| / max|y| <= 2e-3 and NMSE <= 1e-6.  The s field of ds is not read.
- * Reruns are bit-identical.
+ * Per-block products sum_{k in block} a * (q - 8) are exact int32 (i8 MFMA,
+ * centred codes).  The eight blocks of a weight group are combined in int32
+ * with each row's block scales as 13-bit integers relative to the group's
+ * largest (D = rint(d / step), step = max d / 8191), then the group's scale,
+ * step and minimum term are applied in fp32.  So every activation may move by
+ * up to 1/16382 of the largest |x| in its group of 256 on top of Q8_1's own
+ * rounding; measured NMSE ~3e-8 on N(0,1) activations with outliers up to
+ * 1000x.  Results match the fp64 definition to max|dy| / max|y| <= 2e-3 and
+ * NMSE <= 1e-6.  The s field of ds is not read.  Reruns are bit-identical.
  *   qa: device i8 [M][K], 16-byte aligned.  ds: device u16 [M][K/32][2],
  *   4-byte aligned.  qs/sm as for q4_gemv.  y: device fp32 [M][N], 4-byte
  *   aligned.  workspace: at least q4_mmq_workspace_bytes(M, N, K) bytes,
