@@ -124,10 +124,11 @@ __device__ __forceinline__ void convert_x_items(int nitems, int nthr, int base, 
         float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                            fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
         float sum = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
-        sum += __shfl_xor(sum, 1);
-        sum += __shfl_xor(sum, 2);
+        // the chunk's four dwords sit in one lane quad: quad-swap DPP, not LDS
+        amax = fmaxf(amax, dpp_f32<kDppQuadSwap1>(amax));
+        amax = fmaxf(amax, dpp_f32<kDppQuadSwap2>(amax));
+        sum += dpp_f32<kDppQuadSwap1>(sum);
+        sum += dpp_f32<kDppQuadSwap2>(sum);
         const int sc = chunk_exp(amax);
         const float ls = ldexpf(1.0f, -sc), hs = ldexpf(1.0f, -sc - 4);
         // pairs of dword i: (4i, 4i+2) (16+4i, 16+4i+2) (4i+1, 4i+3) (16+4i+1, 16+4i+3)
@@ -142,8 +143,8 @@ __device__ __forceinline__ void convert_x_items(int nitems, int nthr, int base, 
             hw[p] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
         }
         float delta = ldexpf(dl, sc) + ldexpf(dh, sc + 4);
-        delta += __shfl_xor(delta, 1);
-        delta += __shfl_xor(delta, 2);
+        delta += dpp_f32<kDppQuadSwap1>(delta);
+        delta += dpp_f32<kDppQuadSwap2>(delta);
         if (idx < nitems) {
             uint8_t *dst = lds + (idx >> 2) * kChunkLds;
             const int i = idx & 3;
