@@ -459,3 +459,26 @@ def test_mmq_massive_activations(q4, orc):
     x = np.where(rng.random((M, K)) < 0.01, x * 100, x).astype(np.float32)
     x[:, 7] *= 1000
     _mmq_vs_oracle(q4, orc, W, torch.from_numpy(x), "mmq massive activations")
+
+
+def test_mmq_degenerate_groups(q4, orc):
+    # the integer group combination at its edges: rows of zeros (every block
+    # scale 0, step 0), one non-zero block per group, a group whose block
+    # scales span fp16-subnormal to large values, constant weight groups
+    # (scale 0, only the minimum term) and a zero weight row
+    say("mmq degenerate activation and weight groups")
+    M, N, K = 10, 70, 1024
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, 40:72] = rng.standard_normal(32)           # one block of group 0 only
+    x[1, 300] = 5.0                                  # one value in group 1
+    x[2, :32] = 3e4                                  # huge block next to
+    x[2, 32:64] = rng.standard_normal(32) * 1e-6     # an fp16-subnormal d
+    x[3, ::256] = -7e3                               # a spike per group
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    W[0, :256] = 0.125                               # constant group: scale 0
+    W[1] = -0.5                                      # constant row
+    W[2] = 0.0                                       # zero row
+    _mmq_vs_oracle(q4, orc, torch.from_numpy(W), torch.from_numpy(x), "mmq degenerate groups")
