@@ -22,6 +22,8 @@ Algorithmic bytes of a GEMV: packed weights N*K/2 + scales N*K/256*4 + x M*K*4
 + y M*N*4.  Packing (q4_pack) is setup and is not timed.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --pmc-mmq        (Q8_1 + MMQ, M=2048 4096->12288, 3 launches;
+                                         nothing printed)
        python bench.py --pmc-workload   (lm_head GEMV and a 256 MiB copy, 3 launches
                                          each, for hardware-counter runs; prints nothing)
 """
@@ -64,6 +66,8 @@ def parse():
                     help="skip the pp = 256..2048 MMQ sweep and the GEMV/MMQ crossover")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="only launch the lm_head GEMV and a 256 MiB copy (for rocprofv3 --pmc)")
+    ap.add_argument("--pmc-mmq", action="store_true",
+                    help="only launch Q8_1 + MMQ on the M=2048, 4096 -> 12288 layer, 3 times (for rocprofv3 --pmc)")
     return ap.parse_args()
 
 
@@ -118,6 +122,23 @@ def pmc_workload():
     dst = torch.empty_like(src)
     for _ in range(3):
         torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+
+
+def pmc_mmq():
+    """Q8_1 + MMQ on the M = 2048, 4096 -> 12288 prefill layer x3, nothing timed or printed."""
+    import torch
+    import bit_quantized_matmul_q4_amd as q4
+    from bit_quantized_matmul_q4_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    c = wl.MMQ_2048[0]
+    W, x = wl.mmq_case(c["seed"], c["M"], c["N"], c["K"], c["outliers"], dev)
+    qs, sm = q4.q4_pack(W)
+    del W
+    y = torch.empty((c["M"], c["N"]), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        qa, ds = q4.q8_1_quantize(x)
+        q4.q4_mmq_gemm(qa, ds, qs, sm, y=y)
     torch.cuda.synchronize()
 
 
@@ -397,6 +418,9 @@ def main():
               "(the multi-GPU sharding is a design note, not an implementation)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.pmc_mmq:
+        pmc_mmq()
+        return
     if args.pmc_workload:
         pmc_workload()
         return
