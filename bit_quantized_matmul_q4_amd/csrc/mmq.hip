@@ -595,22 +595,51 @@ hipError_t run_tiles(int mode, bool g32, const int8_t *qa, const uint16_t *ds, i
 
 }  // namespace
 
+// The fp16 matrix-core kernels (mmq_f16.hip) take q4_mmq_gemm and its Q8_1
+// variant when their grid of 256 x 128 tiles (one workgroup per CU) keeps
+// the CUs evenly busy: at least 128 tiles and either at most one round of
+// 256 or rounds at least 80 % full.  Elsewhere (small grids, which the K
+// split here keeps busy, and grids that leave most of a last round idle)
+// the int8 kernels here are faster.  Measured on MI355X (q4_mmq_gemm incl.
+// its prep kernels, us): M = 2048 4096 -> 12288 (768 tiles) 275 vs 319;
+// 12288 -> 4096 (256) 240 vs 283; M = 4096 (1536) 512 vs 562; M = 512
+// 2560 -> 9216 (144) 56 vs 62; M = 1024 (384, 1.5 rounds) 153 vs 145;
+// M = 768 (288) 146 vs 136; M = 256 12288 -> 4096 (32) 148 vs 54.
+bool mmq_uses_f16(int64_t M, int64_t N, int64_t K)
+{
+    (void)K;
+    constexpr int64_t kCus = 256;
+    const int64_t tiles = ((M + 255) / 256) * ((N + 127) / 128);
+    if (tiles < kCus / 2) return false;
+    if (tiles <= kCus) return true;
+    const int64_t slots = (tiles + kCus - 1) / kCus * kCus;
+    return tiles * 5 >= slots * 4;
+}
+
 size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < kGroup) return 0;
+    size_t need = 0;
     const SplitCfg sc = choose_split(M, N, (int)K);
-    if (sc.nsplit == 1) return 0;
-    // the largest sub-problem's partials (sub-problems split at < 2 GiB reach)
-    const int64_t n_max = ((kMaxBufferBytes - 1) / (K / 2)) / kTile * kTile;
-    const int64_t m_max = ((kMaxBufferBytes - 1) / K) / kTile * kTile;
-    const int64_t mm = M < m_max ? M : m_max, nn = N < n_max ? N : n_max;
-    return (size_t)sc.nsplit * mm * nn * sizeof(float);
+    if (sc.nsplit > 1) {
+        // the largest sub-problem's partials (sub-problems split at < 2 GiB reach)
+        const int64_t n_max = ((kMaxBufferBytes - 1) / (K / 2)) / kTile * kTile;
+        const int64_t m_max = ((kMaxBufferBytes - 1) / K) / kTile * kTile;
+        const int64_t mm = M < m_max ? M : m_max, nn = N < n_max ? N : n_max;
+        need = (size_t)sc.nsplit * mm * nn * sizeof(float);
+    }
+    if (mmq_uses_f16(M, N, K)) {
+        const size_t f = mmqf_workspace_bytes(M, K);
+        if (f > need) need = f;
+    }
+    return need;
 }
 
 hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                       const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
                       const DeviceInfo &dev, hipStream_t stream)
 {
+    if (mmq_uses_f16(M, N, K)) return launch_mmqf(qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, workspace, stream);
     return run_tiles(kOutY, false, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
                      dev.num_cus, stream);
 }
@@ -627,6 +656,7 @@ hipError_t launch_mmq_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, cons
                            const uint16_t *sm, int64_t N, int K, int8_t *qo, uint16_t *dso,
                            void *workspace, const DeviceInfo &dev, hipStream_t stream)
 {
+    if (mmq_uses_f16(M, N, K)) return launch_mmqf(qa, ds, M, qs, sm, N, K, nullptr, qo, dso, workspace, stream);
     return run_tiles(kOutQ8, false, qa, ds, M, qs, sm, N, K, nullptr, nullptr, qo, dso, workspace,
                      dev.num_cus, stream);
 }

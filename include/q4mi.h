@@ -169,25 +169,47 @@ int q4_mmq_gemm_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8
                     size_t ws_bytes, void *stream);
 
 /*
- * q4_mmq_workspace_bytes -- device workspace q4_mmq_gemm needs for this shape.
- * Pure host function.  Returns 0 for shapes q4_mmq_gemm would reject.
+ * q4_mmq_workspace_bytes -- device workspace q4_mmq_gemm (and
+ * q4_mmq_gemm_q8_1, q4_mmq_gemm_g32) needs for this shape: the fp16
+ * activation image of the fp16 path (2 * K bytes per activation row, at
+ * most 256 MiB + 2 * K * 256 bytes, plus 4 bytes per row), or the K-split
+ * partial sums of the int8 path (0 when K is not split).  Pure host
+ * function.  Returns 0 for shapes q4_mmq_gemm would reject.
  */
 size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * q4_mmq_gemm -- prefill GEMM on Q8_1 activations (the MMQ path of the hipfire
- * note: pre-quantized Q8_1 activations, LDS-staged tiles, integer matrix-core
- * products over 128x128 output tiles):
+ * note: pre-quantized Q8_1 activations, LDS-staged tiles, matrix-core
+ * products over output tiles):
  *     y[m][n] = sum_k (d[m][k/32] * a[m][k]) * (scale[n][k/256] * q[n][k] + minimum[n][k/256])
- * Per-block products sum_{k in block} a * (q - 8) are exact int32 (i8 MFMA,
- * centred codes).  The eight blocks of a weight group are combined in int32
- * with each row's block scales as 13-bit integers relative to the group's
- * largest (D = rint(d / step), step = max d / 8191), then the group's scale,
- * step and minimum term are applied in fp32.  So every activation may move by
- * up to 1/16382 of the largest |x| in its group of 256 on top of Q8_1's own
- * rounding; measured NMSE ~3e-8 on N(0,1) activations with outliers up to
- * 1000x.  Results match the fp64 definition to max|dy| / max|y| <= 2e-3 and
- * NMSE <= 1e-6.  The s field of ds is not read.  Reruns are bit-identical.
+ * Two designs, chosen from the shape alone (so the workspace size, and the
+ * result, depend only on the inputs):
+ *   - fp16 matrix cores, for grids of 256 x 128 output tiles that keep every
+ *     CU evenly busy (at least 128 tiles, and at most 256 or rounds of 256
+ *     at least 80 % full; e.g. M = 2048 at N = 4096 or 12288, M = 512 at
+ *     N = 9216): a prep pass writes each activation as fp16(d * a * 2^f[m]),
+ *     one power of two per row so that the largest is below 2^15; the GEMM
+ *     turns each weight into fp16((scale * q + minimum) * 2^e[n]) in one
+ *     fused multiply-add, one power of two per weight row so that the
+ *     largest is below 2^-6; it multiplies in fp16, sums in fp32 and scales
+ *     y by 2^-(f[m] + e[n]).  Each operand is within 2^-11 relative of its
+ *     exact value; weights below about 2^-7 and activations below about
+ *     2^-28 of their row's largest are fp16 subnormals, exact to 2^-25
+ *     absolute.  Measured
+ *     NMSE ~8e-8, max|dy| / max|y| ~3e-4.
+ *   - int8 matrix cores elsewhere (small grids, which it splits along K):
+ *     per-block products sum_{k in block} a * (q - 8) are exact int32 (i8
+ *     MFMA, centred codes); the eight blocks of a weight group are combined
+ *     in int32 with each row's block scales as 13-bit integers relative to
+ *     the group's largest (D = rint(d / step), step = max d / 8191), then
+ *     the group's scale, step and minimum term are applied in fp32.  So every
+ *     activation may move by up to 1/16382 of the largest |x| in its group of
+ *     256 on top of Q8_1's own rounding; measured NMSE ~3e-8 on N(0,1)
+ *     activations with outliers up to 1000x.
+ * Either way results match the fp64 definition to max|dy| / max|y| <= 2e-3
+ * and NMSE <= 1e-6.  The s field of ds is not read.  Reruns are
+ * bit-identical.
  *   qa: device i8 [M][K], 16-byte aligned.  ds: device u16 [M][K/32][2],
  *   4-byte aligned.  qs/sm as for q4_gemv.  y: device fp32 [M][N], 4-byte
  *   aligned.  workspace: at least q4_mmq_workspace_bytes(M, N, K) bytes,
@@ -211,8 +233,9 @@ int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *
  * s = fp16(d * sum a)).  N must be a multiple of 32.
  *   qa, ds, qs, sm: as for q4_mmq_gemm.  qa_out: device i8 [M][N], 4-byte
  *   aligned.  ds_out: device u16 [M][N/32][2] = (d, s), 4-byte aligned.
- *   workspace: at least q4_mmq_workspace_bytes(M, N, K) bytes (the same
- *   split partials as q4_mmq_gemm), 16-byte aligned, NULL allowed when 0.
+ *   workspace: at least q4_mmq_workspace_bytes(M, N, K) bytes (used as by
+ *   q4_mmq_gemm, which takes the same design for the shape), 16-byte
+ *   aligned, NULL allowed when 0.
  * Errors: Q4_ERR_ARG (also N not a multiple of 32), Q4_ERR_ALIGN,
  * Q4_ERR_WORKSPACE, Q4_ERR_ARCH, Q4_ERR_DEVICE, Q4_ERR_LAUNCH.
  */
@@ -225,8 +248,8 @@ int q4_mmq_gemm_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, const uint
  * checking it bit-exactly (the "keep-quant integer core" the vllm.cpp TG150
  * campaign keeps bit-exact against the CPU, pull request 4, "Design"):
  *     idot[m][n][b] = sum_{k = 32b}^{32b+31} a[m][k] * q[n][k]      (exact int32)
- * It runs the same i8 MFMA tile code as q4_mmq_gemm with an epilogue that
- * stores the per-block sums instead of scaling them.
+ * It runs the same i8 MFMA tile code as q4_mmq_gemm's int8 design with an
+ * epilogue that stores the per-block sums instead of scaling them.
  *   qa: device i8 [M][K], 16-byte aligned.  qs: device u8 [N][K/2], 16-byte
  *   aligned.  idot: device i32 [M][N][K/32], 4-byte aligned (M*N*K/32 entries
  *   must not exceed 2^31).

@@ -482,3 +482,93 @@ def test_mmq_degenerate_groups(q4, orc):
     W[1] = -0.5                                      # constant row
     W[2] = 0.0                                       # zero row
     _mmq_vs_oracle(q4, orc, torch.from_numpy(W), torch.from_numpy(x), "mmq degenerate groups")
+
+
+# ------------------------------------------------- MMQ, fp16 matrix cores ---
+# Shapes whose grid of 256 x 128 tiles fills the GPU run on the fp16 design;
+# its workspace (the fp16 activation image, 2 K bytes per row padded to 256
+# rows, plus 4 bytes per row) tells which design a shape takes.
+
+def f16_workspace(M, K):
+    rows = (M + 255) // 256 * 256
+    return rows * K * 2 + rows * 4
+
+
+def test_mmq_f16_ragged(q4, orc):
+    # 2 x 100 tiles, both edges ragged (300 = 256 + 44 rows, 12700 = 99 * 128 + 28)
+    M, N, K = 300, 12700, 512
+    say("mmq fp16 design M=%d N=%d K=%d" % (M, N, K))
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, K)
+    mmq_check(q4, orc, M, N, K, 71, True, "mmq fp16 ragged")
+
+
+def test_mmq_f16_extremes(q4, orc):
+    # the per-row and per-weight-row powers of two at their edges: the
+    # degenerate activation rows and weight groups of the int8 test, plus
+    # activation rows scaled by 1e-4 and 6e4 and weight rows by 1e-5 and 1e4
+    M, N, K = 260, 12300, 1024
+    say("mmq fp16 design with extreme and degenerate rows M=%d N=%d K=%d" % (M, N, K))
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, K)
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, 40:72] = rng.standard_normal(32)
+    x[2, :32] = 3e4
+    x[2, 32:64] = rng.standard_normal(32) * 1e-6
+    x[3, ::256] = -7e3
+    x[4] *= 1e-4
+    x[5] *= 6e4 / np.abs(x[5]).max()
+    x[257] = 1.0                                     # a row of the ragged tile
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    W[0, :256] = 0.125
+    W[1] = -0.5
+    W[2] = 0.0
+    W[3] *= 1e-5 / 0.02
+    W[4] *= 1e4 / 0.02
+    W[5, 256:512] = 3.0                              # a constant group amid N(0, 0.02)
+    W[N - 1] = 0.25                                  # last (ragged) weight row
+    qs, sm = q4.q4_pack(dev(torch.from_numpy(W)))
+    qa, ds = q4.q8_1_quantize(dev(torch.from_numpy(x)))
+    y = q4.q4_mmq_gemm(qa, ds, qs, sm).cpu().numpy()
+    ref = orc.q4_mmq(qa.cpu().numpy(), ds.cpu().view(torch.int16).numpy().view(np.uint16), qs.cpu().numpy(),
+                     sm.cpu().view(torch.int16).numpy().view(np.uint16), K)
+    assert np.isfinite(y).all()
+    close(y, ref, "mmq fp16 extremes")
+    # the huge rows dominate the global measure: check the ordinary block and
+    # each extreme row and weight row on its own scale as well
+    close(y[6:257, 6:N - 1], ref[6:257, 6:N - 1], "mmq fp16 extremes, ordinary block")
+    for r in (1, 2, 3, 4, 5, 257):
+        close(y[r:r + 1, 6:N - 1], ref[r:r + 1, 6:N - 1], "mmq fp16 extremes, activation row %d" % r)
+    for c in (0, 1, 3, 4, 5, N - 1):
+        close(y[6:257, c:c + 1], ref[6:257, c:c + 1], "mmq fp16 extremes, weight row %d" % c)
+
+
+def test_mmq_f16_q8_1_output_bit_exact(q4, orc):
+    M, N, K = 300, 12288, 512
+    say("mmq fp16 design -> Q8_1 M=%d N=%d K=%d" % (M, N, K))
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, K)
+    W, x = wl.mmq_case(72, M, N, K, True)
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    qo, dso = q4.q4_mmq_gemm_q8_1(qa, ds, qs, sm)
+    y = q4.q4_mmq_gemm(qa, ds, qs, sm)
+    qr, dsr = q4.q8_1_quantize(y)
+    assert torch.equal(qo, qr)
+    assert torch.equal(dso.view(torch.int16), dsr.view(torch.int16))
+    rows = slice(256, 300)
+    oq, ods = orc.q8_1_quantize(y[rows].cpu().numpy())
+    assert np.array_equal(qo[rows].cpu().numpy(), oq)
+    assert np.array_equal(dso[rows].cpu().view(torch.int16).numpy().view(np.uint16), ods)
+
+
+def test_mmq_f16_deterministic(q4, orc):
+    M, N, K = 512, 9216, 2560
+    say("mmq fp16 design rerun determinism M=%d N=%d K=%d" % (M, N, K))
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, K)
+    W, x = wl.mmq_case(73, M, N, K, True)
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    a = q4.q4_mmq_gemm(qa, ds, qs, sm)
+    b = q4.q4_mmq_gemm(qa, ds, qs, sm)
+    assert torch.equal(a, b)
