@@ -29,20 +29,22 @@
 //
 // Design for CDNA4:
 //   * One v_mfma_f32_32x32x16_f16 takes 32 cycles per SIMD, the same as the
-//     int8 32x32x32; per 64-wide K step a wave runs 32 of them and about 75
-//     VALU ops (36 to unpack its weights), so the matrix core, not the VALU,
-//     sets the pace.
+//     int8 32x32x32; per 64-wide K step a wave runs 16 of them against about
+//     40 VALU ops (18 to unpack its weights), so the VALU is not the limit.
 //   * The K order inside an MFMA is free as long as both operands agree, so
 //     each lane unpacks one 32-bit word of packed weights (codes k, k+1, k+2,
 //     k+3 and k+16 .. k+19 of a block) into one MFMA's 8 operand slots with
 //     four masks, and the prep pass writes the activations in that order.
-//   * Tile 128 (n) x 256 (m), 256 threads = 2 x 2 waves of 64 x 128 (2 x 4
-//     MFMA tiles): weights are read straight from global memory (each weight
-//     word feeds 4 MFMAs), the fp16 activation image of a K step (32 KB) is
-//     copied into one of two LDS buffers while the other is consumed.
-//   * The image is laid out per (256-row tile, K step) in LDS order, so the
-//     copy is 8 coalesced 16-byte loads and stores per thread and the LDS
-//     reads (16 bytes per lane, consecutive rows) are conflict-free.
+//   * Tile 256 (m) x 128 (n), 512 threads = 8 waves, two per SIMD: each wave
+//     owns 128 x 64 outputs (4 x 2 MFMA tiles) over half of every K step, and
+//     the two halves are added through LDS at the end.
+//   * Each K step (32 KB of image, 4 KB of packed weights) is loaded straight
+//     into one of 4 LDS stages (no registers in flight); reads and weight
+//     unpacking run one MFMA round ahead of their MFMAs, and the loads are
+//     issued one at a time between MFMAs.
+//   * The image is laid out per (256-row tile, K step) in LDS order: the
+//     loads are contiguous 1 KB per wave and the LDS reads (16 bytes per
+//     lane, consecutive rows) are conflict-free.
 //   * Tiles are mapped so each XCD works on a contiguous run of tiles (m
 //     fastest), which keeps the shared activation and weight tiles in its L2.
 #include "q4mi_device.h"
