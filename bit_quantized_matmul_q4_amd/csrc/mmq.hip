@@ -639,7 +639,8 @@ hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uin
                       const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
                       const DeviceInfo &dev, hipStream_t stream)
 {
-    if (mmq_uses_f16(M, N, K)) return launch_mmqf(qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, workspace, stream);
+    if (mmq_uses_f16(M, N, K))
+        return launch_mmqf(qa, ds, M, qs, sm, N, K, false, y, nullptr, nullptr, workspace, stream);
     return run_tiles(kOutY, false, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
                      dev.num_cus, stream);
 }
@@ -648,6 +649,8 @@ hipError_t launch_mmq_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const
                           const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
                           const DeviceInfo &dev, hipStream_t stream)
 {
+    if (mmq_uses_f16(M, N, K))
+        return launch_mmqf(qa, ds, M, qs, sm, N, K, true, y, nullptr, nullptr, workspace, stream);
     return run_tiles(kOutY, true, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
                      dev.num_cus, stream);
 }
@@ -656,7 +659,8 @@ hipError_t launch_mmq_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, cons
                            const uint16_t *sm, int64_t N, int K, int8_t *qo, uint16_t *dso,
                            void *workspace, const DeviceInfo &dev, hipStream_t stream)
 {
-    if (mmq_uses_f16(M, N, K)) return launch_mmqf(qa, ds, M, qs, sm, N, K, nullptr, qo, dso, workspace, stream);
+    if (mmq_uses_f16(M, N, K))
+        return launch_mmqf(qa, ds, M, qs, sm, N, K, false, nullptr, qo, dso, workspace, stream);
     return run_tiles(kOutQ8, false, qa, ds, M, qs, sm, N, K, nullptr, nullptr, qo, dso, workspace,
                      dev.num_cus, stream);
 }

@@ -62,8 +62,12 @@ constexpr int kStepVecs = 8 * kFm; // 16-byte vectors of the image per (tile, st
 constexpr int kGemmThreads = 512;
 constexpr int kStages = 4;                      // K steps in LDS at once
 constexpr int kStageVecs = kStepVecs + 2 * kFn; // image + packed weights of a step
-constexpr int kLdsVecs = kStages * kStageVecs;  // 144 KB
+constexpr int kSmVecs32 = 2 * kFn / 4;          // group 32: the step's (scale, minimum) pairs
+// 144 KB; with group-32 weights 148 KB
+__host__ __device__ constexpr int stage_vecs(bool g32) { return kStageVecs + (g32 ? kSmVecs32 : 0); }
+constexpr int kLdsVecs = kStages * kStageVecs;
 static_assert(kLdsVecs >= 8 * 1024, "the K-half exchange needs 16 KB per wave");
+static_assert(kStages * stage_vecs(true) * 16 + 3 * kFn * 4 + kFn * 8 <= 160 * 1024, "LDS of a CU");
 // largest activation image per launch; bigger M runs in row chunks
 constexpr int64_t kImageMaxBytes = (int64_t)256 << 20;
 
@@ -216,7 +220,9 @@ __device__ __forceinline__ void wait_vm_barrier()
 // weight rows 64 wn .. 64 wn + 63 (two MFMA tiles) x activation rows
 // 128 wm .. 128 wm + 127 (four) over half of each K step, MFMAs t = 2 wk and
 // 2 wk + 1; the two K halves are added through LDS at the end.
-template <int kMode>
+// kG32: group-32 weights, one (scale, minimum) pair per Q8_1 block; the
+// pairs of a step travel with it and the operand constants change per step.
+template <int kMode, bool kG32 = false>
 __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     const uint4 *__restrict__ img, uint32_t img_bytes, const float *__restrict__ fs,
     const uint8_t *__restrict__ qs, const uint32_t *__restrict__ sm, float *__restrict__ y,
@@ -225,9 +231,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
 {
     // kStages K steps in flight (image + packed weights each), the (scale,
     // minimum) words of two groups; at the end, the K-half exchange
-    __shared__ int4_t lds[kLdsVecs];
+    constexpr int kSV = stage_vecs(kG32);
+    __shared__ int4_t lds[kStages * kSV];
     __shared__ uint32_t sSM[2][kFn];
     __shared__ float sScale[kFn];  // 2^-E per weight row of the tile
+    __shared__ int sE[kFn];        // E per weight row of the tile (group 32)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar arithmetic
@@ -237,31 +245,56 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     const int mt = tile % tiles_m, nt = tile / tiles_m;
     const int n0 = nt * kFn, m0 = mt * kFm;
     const int S = K / kFk, G = K / kGroup;
+    const int P = kG32 ? K / kBlock : G;  // (scale, minimum) pairs per weight row
     const uint32_t rowq = (uint32_t)K / 2;
     const rsrc_t r_img = make_rsrc(img, img_bytes);
     const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowq);
-    const rsrc_t r_sm = make_rsrc(sm, (uint32_t)N * G * 4u);
+    const rsrc_t r_sm = make_rsrc(sm, (uint32_t)N * P * 4u);
     uint32_t nrow[2];  // this lane's weight row in each MFMA tile (past N: loads give 0)
 #pragma unroll
     for (int j = 0; j < 2; ++j) nrow[j] = (uint32_t)(n0 + wn * 64 + 32 * j + l32);
 
     // ---- per weight row: E with (max |minimum| + 15 |scale|) * 2^E in [2^-7, 2^-6) ----
-    int E[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        float wmax = 0.0f;
-        for (int g = h; g < G; g += 2) {
-            const uint32_t v = buf_load4(r_sm, (nrow[j] * G + g) * 4u);
-            wmax = fmaxf(wmax, fabsf(f16_bits_to_f32(v >> 16)) + 15.0f * fabsf(f16_bits_to_f32(v & 0xFFFFu)));
-        }
-        wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
+    auto pair_bound = [](uint32_t v) {
+        return fabsf(f16_bits_to_f32(v >> 16)) + 15.0f * fabsf(f16_bits_to_f32(v & 0xFFFFu));
+    };
+    auto exponent_of = [](float wmax) {
         int e = 0;
-        E[j] = 0;
         if (wmax > 0.0f && wmax <= 3.0e38f) {
             frexpf(wmax, &e);
-            E[j] = -6 - e;
+            return -6 - e;
         }
-        if (h == 0 && wk == 0 && wm == 0) sScale[wn * 64 + 32 * j + l32] = ldexpf(1.0f, -E[j]);
+        return 0;
+    };
+    int E[2];
+    if (kG32) {
+        // K / 32 pairs per row: four threads per row, 16-byte reads
+        const int r = tid >> 2, q = tid & 3;
+        const uint32_t base = (uint32_t)(n0 + r) * (uint32_t)P * 4u;
+        float wmax = 0.0f;
+        for (int i = q; 4 * i < P; i += 4) {  // P = K / 32 is a multiple of 8
+            const uint4 v = buf_load16(r_sm, base + 16u * (uint32_t)i);
+            wmax = fmaxf(fmaxf(wmax, fmaxf(pair_bound(v.x), pair_bound(v.y))), fmaxf(pair_bound(v.z), pair_bound(v.w)));
+        }
+        wmax = fmaxf(wmax, dpp_f32<kDppQuadSwap1>(wmax));
+        wmax = fmaxf(wmax, dpp_f32<kDppQuadSwap2>(wmax));
+        if (q == 0) {
+            const int e = exponent_of(wmax);
+            sE[r] = e;
+            sScale[r] = ldexpf(1.0f, -e);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) E[j] = sE[wn * 64 + 32 * j + l32];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float wmax = 0.0f;
+            for (int g = h; g < G; g += 2) wmax = fmaxf(wmax, pair_bound(buf_load4(r_sm, (nrow[j] * G + g) * 4u)));
+            wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
+            E[j] = exponent_of(wmax);
+            if (h == 0 && wk == 0 && wm == 0) sScale[wn * 64 + 32 * j + l32] = ldexpf(1.0f, -E[j]);
+        }
     }
 
     // ---- loads straight into LDS (no registers in flight) ----
@@ -283,21 +316,24 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     for (int i = 0; i < 4; ++i) img_v[i] = (uint32_t)(wave * 256 + i * 64 + lane) * 16u;
     const uint32_t wcol = (uint32_t)((wave * 64 + lane) & 127), wblk = (uint32_t)((wave * 64 + lane) >> 7);
     const uint32_t wts_v = (n0 + wcol) * rowq + wblk * 16u;
+    const uint32_t sm32_v = (n0 + wcol) * (uint32_t)P * 4u + wblk * 4u;  // group 32
     // The loads of step s come in pieces: piece p < 4 is image vectors
     // 256 wave + 64 p .. + 63, piece 4 the weights (waves 0-3).  Part 0 of a
     // step is pieces 0, 1, 4, part 1 pieces 2, 3.
     auto issue_piece = [&](int s, int p) {
         const int sl = min(s, S - 1);
-        const uint32_t stage = lds0 + (uint32_t)((s % kStages) * kStageVecs) * 16u;
+        const uint32_t stage = lds0 + (uint32_t)((s % kStages) * kSV) * 16u;
         if (p < 4) {
             const uint32_t goff = (uint32_t)((mt * S + sl) * kStepVecs) * 16u;
             dma16(r_img, img_v[p], goff, stage + (uint32_t)(wave * 256 + p * 64) * 16u);
         } else if (wave < 4) {
             dma16(r_qs, wts_v, (uint32_t)sl * 32u, stage + (uint32_t)(kStepVecs + wave * 64) * 16u);
+            if (kG32)  // the step's pairs as [block][row]
+                dma4(r_sm, sm32_v, (uint32_t)sl * 8u, stage + (uint32_t)(kStageVecs * 16 + wave * 256));
         }
     };
     auto issue_sm = [&](int g) {
-        if (wave < 2 && g < G) {
+        if (!kG32 && wave < 2 && g < G) {
             const uint32_t c = (uint32_t)(wave * 64 + lane);
             dma4(r_sm, (n0 + c) * G * 4u, (uint32_t)g * 4u, sm0 + (uint32_t)((g & 1) * kFn + wave * 64) * 4u);
         }
@@ -315,7 +351,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     // this wave's two weight words per MFMA tile (bytes 8 wk .. 8 wk + 7 of
     // the (row, block h) vector)
     auto read_frags = [&](int s, int tl, f16x8 (&bv)[4]) {
-        const int4_t *act = lds + (s % kStages) * kStageVecs + wm * 128 + l32;
+        const int4_t *act = lds + (s % kStages) * kSV + wm * 128 + l32;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             bv[i] = __builtin_bit_cast(f16x8, act[(2 * (2 * wk + tl) + h) * kFm + 32 * i]);
@@ -323,19 +359,21 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     auto read_wts = [&](int s, int2_t (&wq)[2]) {
         // the stage holds the weight vectors as [block][row]: 32 consecutive
         // rows per half-wave, conflict-free 16-byte reads
-        const int4_t *wv = lds + (s % kStages) * kStageVecs + kStepVecs + h * kFn + wn * 64 + l32;
+        const int4_t *wv = lds + (s % kStages) * kSV + kStepVecs + h * kFn + wn * 64 + l32;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int4_t v = wv[32 * j];
             wq[j] = wk ? int2_t{v.z, v.w} : int2_t{v.x, v.y};
         }
     };
-    // the weight group's (s' * 2^24, s' * 2^20, mn') as fp16 pairs
+    // the weight group's (s' * 2^24, s' * 2^20, mn') as fp16 pairs; with
+    // group-32 weights, the pair of this lane's block h of step g
     half2_t cs[2], cs16[2], cmn[2];
     auto group_consts = [&](int g) {
+        const uint32_t *sm32 = reinterpret_cast<const uint32_t *>(lds + (g % kStages) * kSV + kStageVecs);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint32_t w = sSM[g & 1][wn * 64 + 32 * j + l32];
+            const uint32_t w = kG32 ? sm32[h * kFn + wn * 64 + 32 * j + l32] : sSM[g & 1][wn * 64 + 32 * j + l32];
             const float sc = f16_bits_to_f32(w & 0xFFFFu), mn = f16_bits_to_f32(w >> 16);
             const _Float16 a = (_Float16)ldexpf(sc, E[j] + 24), b = (_Float16)ldexpf(sc, E[j] + 20),
                            c = (_Float16)ldexpf(mn, E[j]);
@@ -411,7 +449,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
         unpack(1, wq, avB);
         wait_vm_barrier<4 * (kStages - 3)>();
         if ((s & 3) == 0) issue_sm((s >> 2) + 1);
-        if (((s + 1) & 3) == 0 && s + 1 < S) group_consts((s + 1) >> 2);
+        if (kG32)
+            group_consts(s + 1);  // (s + 1 = S reads a stage's stale pairs, unused)
+        else if (((s + 1) & 3) == 0 && s + 1 < S)
+            group_consts((s + 1) >> 2);
         read_wts(s + 1, wq);
         read_frags(s + 1, 0, bvA);
         // round 1, with part 0 of step s + kStages - 1
@@ -540,10 +581,12 @@ size_t mmqf_workspace_bytes(int64_t M, int64_t K)
 }
 
 hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
-                       const uint16_t *sm, int64_t N, int K, float *y, int8_t *qo, uint16_t *dso,
+                       const uint16_t *sm, int64_t N, int K, bool g32, float *y, int8_t *qo, uint16_t *dso,
                        void *workspace, hipStream_t stream)
 {
-    const int B = K / kBlock, G = K / kGroup, S = K / kFk;
+    const int B = K / kBlock, S = K / kFk;
+    const int P = g32 ? B : K / kGroup;  // (scale, minimum) pairs per weight row
+    if (g32 && !y) return hipErrorInvalidValue;  // group 32: fp32 output only
     const int64_t rows_max = chunk_rows(M, K);
     uint4 *img = static_cast<uint4 *>(workspace);
     float *fs = reinterpret_cast<float *>(static_cast<char *>(workspace) + rows_max * K * 2);
@@ -569,12 +612,17 @@ hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const ui
                 float *y0 = y + m0 * N + n0;
                 const int vec_store = (N % 4 == 0) && (nn % 4 == 0) &&
                                       ((reinterpret_cast<uintptr_t>(y0) & 15) == 0);
-                hipLaunchKernelGGL(k_mmqf<kFOutY>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, img, img_bytes, fs,
-                                   qs + n0 * (K / 2), sm32 + n0 * G, y0, (int8_t *)nullptr, (uint32_t *)nullptr,
-                                   (int)mm, (int)nn, K, tiles_m, N, vec_store);
+                if (g32)
+                    hipLaunchKernelGGL((k_mmqf<kFOutY, true>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream,
+                                       img, img_bytes, fs, qs + n0 * (K / 2), sm32 + n0 * P, y0, (int8_t *)nullptr,
+                                       (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, N, vec_store);
+                else
+                    hipLaunchKernelGGL(k_mmqf<kFOutY>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, img,
+                                       img_bytes, fs, qs + n0 * (K / 2), sm32 + n0 * P, y0, (int8_t *)nullptr,
+                                       (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, N, vec_store);
             } else {
                 hipLaunchKernelGGL(k_mmqf<kFOutQ8>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, img, img_bytes, fs,
-                                   qs + n0 * (K / 2), sm32 + n0 * G, (float *)nullptr, qo + m0 * N + n0,
+                                   qs + n0 * (K / 2), sm32 + n0 * P, (float *)nullptr, qo + m0 * N + n0,
                                    dso32 + m0 * (N / kBlock) + n0 / kBlock, (int)mm, (int)nn, K, tiles_m, N, 0);
             }
             const hipError_t e = hipGetLastError();

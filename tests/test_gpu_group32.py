@@ -158,3 +158,25 @@ def test_mmq_g32_equal_pairs_match_g256(q4, orc):
     sm32 = sm.repeat_interleave(8, dim=1).contiguous()
     close(q4.q4_mmq_gemm_g32(qa, ds, qs, sm32).cpu().numpy(), q4.q4_mmq_gemm(qa, ds, qs, sm).cpu().numpy(),
           "mmq g32 repeated vs g256")
+
+
+# Shapes whose grid fills the GPU run on the fp16 matrix-core design, where
+# each lane's (scale, minimum) pair changes every Q8_1 block.
+
+def test_mmq_g32_f16_ragged(q4, orc):
+    M, N, K = 300, 12700, 512
+    say("mmq g32, fp16 design, M=%d N=%d K=%d" % (M, N, K))
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == (M + 255) // 256 * 256 * (2 * K + 4)
+    mmq_g32_check(q4, orc, M, N, K, 74, True, "mmq g32 fp16 ragged")
+
+
+def test_mmq_g32_f16_equal_pairs_match_g256(q4, orc):
+    # the same pair in all eight blocks of each group: the operands are the
+    # group-256 design's, bit for bit, and so is the result
+    M, N, K = 300, 12288, 1024
+    say("mmq g32 with repeated pairs vs g256, fp16 design, M=%d N=%d K=%d" % (M, N, K))
+    W, x = wl.mmq_case(75, M, N, K, True)
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    sm32 = sm.repeat_interleave(8, dim=1).contiguous()
+    assert torch.equal(q4.q4_mmq_gemm_g32(qa, ds, qs, sm32), q4.q4_mmq_gemm(qa, ds, qs, sm))
