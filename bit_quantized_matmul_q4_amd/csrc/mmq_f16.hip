@@ -29,22 +29,22 @@
 //
 // Design for CDNA4:
 //   * One v_mfma_f32_32x32x16_f16 takes 32 cycles per SIMD, the same as the
-//     int8 32x32x32; per 64-wide K step a wave runs 16 of them against about
-//     40 VALU ops (18 to unpack its weights), so the VALU is not the limit.
+//     int8 32x32x32; per 64-wide K step a computing wave runs 32 of them
+//     against about 40 VALU ops (36 to unpack its weights), so the VALU is
+//     not the limit.
 //   * The K order inside an MFMA is free as long as both operands agree, so
 //     each lane unpacks one 32-bit word of packed weights (codes k, k+1, k+2,
 //     k+3 and k+16 .. k+19 of a block) into one MFMA's 8 operand slots with
 //     four masks, and the prep pass writes the activations in that order.
-//   * Tile 256 (m) x 128 (n), 512 threads = 8 waves, two per SIMD: each wave
-//     owns 128 x 64 outputs (4 x 2 MFMA tiles) over half of every K step, and
-//     the two halves are added through LDS at the end.
+//   * Tile 256 (m) x 128 (n), 512 threads = 8 waves, two per SIMD: one wave
+//     per SIMD loads, one computes 128 x 64 outputs (4 x 2 MFMA tiles).
 //   * Each K step (32 KB of image, 4 KB of packed weights) is loaded straight
-//     into one of 4 LDS stages (no registers in flight); reads and weight
-//     unpacking run one MFMA round ahead of their MFMAs, and the loads are
-//     issued one at a time between MFMAs.
+//     into one of 4 LDS stages (no registers in flight, two steps ahead);
+//     the computing waves read and unpack each MFMA round's operands during
+//     the round before.
 //   * The image is laid out per (256-row tile, K step) in LDS order: the
-//     loads are contiguous 1 KB per wave and the LDS reads (16 bytes per
-//     lane, consecutive rows) are conflict-free.
+//     loads are contiguous 1 KB per instruction and the LDS reads (16 bytes
+//     per lane, consecutive rows) are conflict-free.
 //   * Tiles are mapped so each XCD works on a contiguous run of tiles (m
 //     fastest), which keeps the shared activation and weight tiles in its L2.
 #include "q4mi_device.h"
@@ -63,10 +63,8 @@ constexpr int kGemmThreads = 512;
 constexpr int kStages = 4;                      // K steps in LDS at once
 constexpr int kStageVecs = kStepVecs + 2 * kFn; // image + packed weights of a step
 constexpr int kSmVecs32 = 2 * kFn / 4;          // group 32: the step's (scale, minimum) pairs
-// 144 KB; with group-32 weights 148 KB
+// 144 KB of stages; with group-32 weights 148 KB
 __host__ __device__ constexpr int stage_vecs(bool g32) { return kStageVecs + (g32 ? kSmVecs32 : 0); }
-constexpr int kLdsVecs = kStages * kStageVecs;
-static_assert(kLdsVecs >= 8 * 1024, "the K-half exchange needs 16 KB per wave");
 static_assert(kStages * stage_vecs(true) * 16 + 3 * kFn * 4 + kFn * 8 <= 160 * 1024, "LDS of a CU");
 // largest activation image per launch; bigger M runs in row chunks
 constexpr int64_t kImageMaxBytes = (int64_t)256 << 20;
@@ -74,7 +72,6 @@ constexpr int64_t kImageMaxBytes = (int64_t)256 << 20;
 enum { kFOutY = 0, kFOutQ8 = 1 };
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef int int2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int xcd_tile_f(int pid, int ntiles)
 {
@@ -158,20 +155,6 @@ __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restri
     }
 }
 
-template <int v>
-struct IC {
-    static constexpr int value = v;
-};
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F &&f)
-{
-    if constexpr (I < N) {
-        f(IC<I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
 // LDS byte address of a __shared__ object
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
@@ -213,15 +196,15 @@ __device__ __forceinline__ void wait_vm_barrier()
 // y (row stride ldy) for activation rows [0, M) and weight rows [0, N) of
 // this sub-problem; img/fs are its activation image and row factors.
 // Output modes: fp32 y, or y quantized to Q8_1 along n (qo int8 [M][ldy],
-// dso [M][ldy/32]) as q8_1_quantize would do it.
+// dso [M][ldy/32]) as q8_1_quantize would do it.  kG32: group-32 weights,
+// one (scale, minimum) pair per Q8_1 block; the pairs of a step travel with
+// it and the operand constants change per step.
 //
-// 512 threads = 8 waves, two per SIMD so that one's waits (LDS, memory,
-// barrier) are covered by the other's MFMAs: wave (wk, wm, wn) computes
-// weight rows 64 wn .. 64 wn + 63 (two MFMA tiles) x activation rows
-// 128 wm .. 128 wm + 127 (four) over half of each K step, MFMAs t = 2 wk and
-// 2 wk + 1; the two K halves are added through LDS at the end.
-// kG32: group-32 weights, one (scale, minimum) pair per Q8_1 block; the
-// pairs of a step travel with it and the operand constants change per step.
+// 512 threads = 8 waves, two per SIMD.  Waves 4-7 (one per SIMD) only load
+// K steps into LDS; waves 0-3 (one per SIMD) only compute, wave (wm, wn)
+// owning activation rows 128 wm .. 128 wm + 127 (four MFMA tiles) x weight
+// rows 64 wn .. 64 wn + 63 (two) over whole K steps (4 MFMA rounds per
+// step), so the computing waves never issue a vector-memory instruction.
 template <int kMode, bool kG32 = false>
 __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     const uint4 *__restrict__ img, uint32_t img_bytes, const float *__restrict__ fs,
@@ -229,32 +212,30 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     int8_t *__restrict__ qo, uint32_t *__restrict__ dso, int M, int N, int K, int tiles_m, int64_t ldy,
     int vec_store)
 {
-    // kStages K steps in flight (image + packed weights each), the (scale,
-    // minimum) words of two groups; at the end, the K-half exchange
     constexpr int kSV = stage_vecs(kG32);
     __shared__ int4_t lds[kStages * kSV];
     __shared__ uint32_t sSM[2][kFn];
-    __shared__ float sScale[kFn];  // 2^-E per weight row of the tile
-    __shared__ int sE[kFn];        // E per weight row of the tile (group 32)
+    __shared__ float sScale[kFn];
+    __shared__ int sE[kFn];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar arithmetic
-    const int wn = wave & 1, wm = (wave >> 1) & 1, wk = wave >> 2;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool consumer = wave < 4;
+    const int wn = wave & 1, wm = (wave >> 1) & 1, pw = wave - 4;
     const int l32 = lane & 31, h = lane >> 5;
     const int tile = xcd_tile_f(blockIdx.x, gridDim.x);
     const int mt = tile % tiles_m, nt = tile / tiles_m;
     const int n0 = nt * kFn, m0 = mt * kFm;
     const int S = K / kFk, G = K / kGroup;
-    const int P = kG32 ? K / kBlock : G;  // (scale, minimum) pairs per weight row
+    const int P = kG32 ? K / kBlock : G;
     const uint32_t rowq = (uint32_t)K / 2;
     const rsrc_t r_img = make_rsrc(img, img_bytes);
     const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowq);
     const rsrc_t r_sm = make_rsrc(sm, (uint32_t)N * P * 4u);
-    uint32_t nrow[2];  // this lane's weight row in each MFMA tile (past N: loads give 0)
+    uint32_t nrow[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) nrow[j] = (uint32_t)(n0 + wn * 64 + 32 * j + l32);
 
-    // ---- per weight row: E with (max |minimum| + 15 |scale|) * 2^E in [2^-7, 2^-6) ----
     auto pair_bound = [](uint32_t v) {
         return fabsf(f16_bits_to_f32(v >> 16)) + 15.0f * fabsf(f16_bits_to_f32(v & 0xFFFFu));
     };
@@ -266,13 +247,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
         }
         return 0;
     };
-    int E[2];
+    int E[2] = {0, 0};
     if (kG32) {
-        // K / 32 pairs per row: four threads per row, 16-byte reads
         const int r = tid >> 2, q = tid & 3;
         const uint32_t base = (uint32_t)(n0 + r) * (uint32_t)P * 4u;
         float wmax = 0.0f;
-        for (int i = q; 4 * i < P; i += 4) {  // P = K / 32 is a multiple of 8
+        for (int i = q; 4 * i < P; i += 4) {
             const uint4 v = buf_load16(r_sm, base + 16u * (uint32_t)i);
             wmax = fmaxf(fmaxf(wmax, fmaxf(pair_bound(v.x), pair_bound(v.y))), fmaxf(pair_bound(v.z), pair_bound(v.w)));
         }
@@ -286,59 +266,62 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 2; ++j) E[j] = sE[wn * 64 + 32 * j + l32];
-    } else {
+    } else if (consumer) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             float wmax = 0.0f;
             for (int g = h; g < G; g += 2) wmax = fmaxf(wmax, pair_bound(buf_load4(r_sm, (nrow[j] * G + g) * 4u)));
             wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
             E[j] = exponent_of(wmax);
-            if (h == 0 && wk == 0 && wm == 0) sScale[wn * 64 + 32 * j + l32] = ldexpf(1.0f, -E[j]);
+            if (h == 0 && wm == 0) sScale[wn * 64 + 32 * j + l32] = ldexpf(1.0f, -E[j]);
         }
     }
 
-    // ---- loads straight into LDS (no registers in flight) ----
-    // Step s lives in stage s % kStages: 2048 image vectors (wave w copies
-    // [256 w, 256 w + 256)), then the tile's packed weights of the step, one
-    // 16-byte vector per (weight row, Q8_1 block) (waves 0-3): at least 4
-    // loads per wave per step.  The loads of step s + kStages - 1 are issued
-    // in the middle of step s, into the stage of step s - 1, right after a
-    // wait for step s + 1 (all but the last step's loads done) and a
-    // barrier, which also puts every wave past its reads of step s - 1.
-    // Loads past the last step repeat the last step (unused), so the count
-    // holds to the end.  Group g's (scale, minimum) words (waves 0-1) are
-    // loaded with the first step of group g - 1.
     const uint32_t lds0 = lds_addr(lds);
     const uint32_t sm0 = lds_addr(&sSM[0][0]);
-    // per-lane parts of the load offsets; the step enters as a scalar offset
-    uint32_t img_v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) img_v[i] = (uint32_t)(wave * 256 + i * 64 + lane) * 16u;
-    const uint32_t wcol = (uint32_t)((wave * 64 + lane) & 127), wblk = (uint32_t)((wave * 64 + lane) >> 7);
-    const uint32_t wts_v = (n0 + wcol) * rowq + wblk * 16u;
-    const uint32_t sm32_v = (n0 + wcol) * (uint32_t)P * 4u + wblk * 4u;  // group 32
-    // The loads of step s come in pieces: piece p < 4 is image vectors
-    // 256 wave + 64 p .. + 63, piece 4 the weights (waves 0-3).  Part 0 of a
-    // step is pieces 0, 1, 4, part 1 pieces 2, 3.
-    auto issue_piece = [&](int s, int p) {
-        const int sl = min(s, S - 1);
-        const uint32_t stage = lds0 + (uint32_t)((s % kStages) * kSV) * 16u;
-        if (p < 4) {
-            const uint32_t goff = (uint32_t)((mt * S + sl) * kStepVecs) * 16u;
-            dma16(r_img, img_v[p], goff, stage + (uint32_t)(wave * 256 + p * 64) * 16u);
-        } else if (wave < 4) {
-            dma16(r_qs, wts_v, (uint32_t)sl * 32u, stage + (uint32_t)(kStepVecs + wave * 64) * 16u);
-            if (kG32)  // the step's pairs as [block][row]
-                dma4(r_sm, sm32_v, (uint32_t)sl * 8u, stage + (uint32_t)(kStageVecs * 16 + wave * 256));
-        }
-    };
-    auto issue_sm = [&](int g) {
-        if (!kG32 && wave < 2 && g < G) {
-            const uint32_t c = (uint32_t)(wave * 64 + lane);
-            dma4(r_sm, (n0 + c) * G * 4u, (uint32_t)g * 4u, sm0 + (uint32_t)((g & 1) * kFn + wave * 64) * 4u);
-        }
-    };
 
+    if (!consumer) {
+        // ---- producer: step s in stage s % kStages; 8 image pieces (2048
+        // vectors / 4 producers), one weight piece, with group-32 weights one
+        // piece of pairs: at least 9 loads per step.  Barrier B_s (the
+        // consumers' barrier between rounds 2 and 3 of step s) needs step
+        // s + 1 in LDS; after it, step s + kStages - 1 goes into the stage of
+        // step s - 1, whose reads the consumers finished before B_s. ----
+        const uint32_t wcol = (uint32_t)((pw * 64 + lane) & 127), wblk = (uint32_t)((pw * 64 + lane) >> 7);
+        const uint32_t wts_v = (n0 + wcol) * rowq + wblk * 16u;
+        const uint32_t sm32_v = (n0 + wcol) * (uint32_t)P * 4u + wblk * 4u;
+        auto issue = [&](int s) {
+            const int sl = min(s, S - 1);
+            const uint32_t stage = lds0 + (uint32_t)((s % kStages) * kSV) * 16u;
+            const uint32_t goff = (uint32_t)((mt * S + sl) * kStepVecs) * 16u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t v = (uint32_t)(pw * 512 + i * 64);
+                dma16(r_img, (v + lane) * 16u, goff, stage + v * 16u);
+            }
+            dma16(r_qs, wts_v, (uint32_t)sl * 32u, stage + (uint32_t)(kStepVecs + pw * 64) * 16u);
+            if (kG32) dma4(r_sm, sm32_v, (uint32_t)sl * 8u, stage + (uint32_t)(kStageVecs * 16 + pw * 256));
+        };
+        auto issue_sm = [&](int g) {
+            if (!kG32 && pw < 2 && g < G) {
+                const uint32_t c = (uint32_t)(pw * 64 + lane);
+                dma4(r_sm, (n0 + c) * G * 4u, (uint32_t)g * 4u, sm0 + (uint32_t)((g & 1) * kFn + pw * 64) * 4u);
+            }
+        };
+        issue_sm(0);
+        for (int s = 0; s < kStages - 2; ++s) issue(s);
+        wait_vm_barrier<9 * (kStages - 3)>();  // B_init: step 0
+        issue(kStages - 2);
+        for (int s = 0; s < S; ++s) {
+            wait_vm_barrier<9 * (kStages - 3)>();  // B_s: step s + 1
+            issue(s + kStages - 1);
+            if ((s & 3) == 0) issue_sm((s >> 2) + 1);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
+    }
+
+    // ---- consumer ----
     float16_t acc[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -346,34 +329,23 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
-
-    // activation fragments of MFMA round tl (t = 2 wk + tl) of step s, and
-    // this wave's two weight words per MFMA tile (bytes 8 wk .. 8 wk + 7 of
-    // the (row, block h) vector)
-    auto read_frags = [&](int s, int tl, f16x8 (&bv)[4]) {
+    auto read_frags = [&](int s, int t, f16x8 (&bv)[4]) {
         const int4_t *act = lds + (s % kStages) * kSV + wm * 128 + l32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            bv[i] = __builtin_bit_cast(f16x8, act[(2 * (2 * wk + tl) + h) * kFm + 32 * i]);
+        for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(f16x8, act[(2 * t + h) * kFm + 32 * i]);
     };
-    auto read_wts = [&](int s, int2_t (&wq)[2]) {
-        // the stage holds the weight vectors as [block][row]: 32 consecutive
-        // rows per half-wave, conflict-free 16-byte reads
+    auto read_wts = [&](int s, int4_t (&wq)[2]) {
         const int4_t *wv = lds + (s % kStages) * kSV + kStepVecs + h * kFn + wn * 64 + l32;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int4_t v = wv[32 * j];
-            wq[j] = wk ? int2_t{v.z, v.w} : int2_t{v.x, v.y};
-        }
+        for (int j = 0; j < 2; ++j) wq[j] = wv[32 * j];
     };
-    // the weight group's (s' * 2^24, s' * 2^20, mn') as fp16 pairs; with
-    // group-32 weights, the pair of this lane's block h of step g
     half2_t cs[2], cs16[2], cmn[2];
-    auto group_consts = [&](int g) {
-        const uint32_t *sm32 = reinterpret_cast<const uint32_t *>(lds + (g % kStages) * kSV + kStageVecs);
+    auto consts = [&](int s) {
+        // group 256: the constants of step s's group; group 32: of step s
+        const uint32_t *sm32 = reinterpret_cast<const uint32_t *>(lds + (s % kStages) * kSV + kStageVecs);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint32_t w = kG32 ? sm32[h * kFn + wn * 64 + 32 * j + l32] : sSM[g & 1][wn * 64 + 32 * j + l32];
+            const uint32_t w = kG32 ? sm32[h * kFn + wn * 64 + 32 * j + l32] : sSM[(s >> 2) & 1][wn * 64 + 32 * j + l32];
             const float sc = f16_bits_to_f32(w & 0xFFFFu), mn = f16_bits_to_f32(w >> 16);
             const _Float16 a = (_Float16)ldexpf(sc, E[j] + 24), b = (_Float16)ldexpf(sc, E[j] + 20),
                            c = (_Float16)ldexpf(mn, E[j]);
@@ -382,12 +354,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
             cmn[j] = half2_t{c, c};
         }
     };
-    // the weight operands of MFMA round tl: codes of bytes 0 and 2 (low,
-    // high nibble), then bytes 1 and 3 of the round's 32-bit word
-    auto unpack = [&](int tl, const int2_t (&wq)[2], f16x8 (&av)[2]) {
+    auto unpack = [&](int t, const int4_t (&wq)[2], f16x8 (&av)[2]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint32_t w = (uint32_t)wq[j][tl], w8 = w >> 8;
+            const uint32_t w = (uint32_t)wq[j][t], w8 = w >> 8;
             const half2_t p0 = __builtin_elementwise_fma(as_half2(w & 0x000F000Fu), cs[j], cmn[j]);
             const half2_t p1 = __builtin_elementwise_fma(as_half2(w & 0x00F000F0u), cs16[j], cmn[j]);
             const half2_t p2 = __builtin_elementwise_fma(as_half2(w8 & 0x000F000Fu), cs[j], cmn[j]);
@@ -395,164 +365,107 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
             av[j] = f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
         }
     };
-    // a round's 8 MFMAs with up to 3 load pieces placed after MFMAs 2, 4
-    // and 6, so that loads enter the memory pipeline one at a time
-    auto mfmas = [&](const f16x8 (&av)[2], const f16x8 (&bv)[4], int s, int p0, int p1, int p2) {
+    auto mfmas = [&](const f16x8 (&av)[2], const f16x8 (&bv)[4]) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int j = k >> 2, i = k & 3;
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[j], bv[i], acc[j][i], 0, 0, 0);
-            if (k == 1 || k == 3 || k == 5) {
-                const int p = k == 1 ? p0 : (k == 3 ? p1 : p2);
-                if (p >= 0) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue_piece(s, p);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[j], bv[i], acc[j][i], 0, 0, 0);
     };
 
-    // Prologue: steps 0 .. kStages - 3 and part 0 of step kStages - 2 in
-    // flight; wait for step 0, read it and unpack its round-0 weights.
-    // Step s: round 0's MFMAs, interleaved with part 1 of step s + kStages
-    // - 2 (into the stage of step s - 2), while round 1's weights are
-    // unpacked; wait for step s + 1 (after part 1 of step s + 1 come at
-    // least part 0 and part 1 of step s + 2: 4 loads) and barrier (every
-    // wave is past its reads of step s - 1); read step s + 1's weights and
-    // round-0 fragments; round 1's MFMAs, interleaved with part 0 of step
-    // s + kStages - 1 (into the stage of step s - 1), while step s + 1's
-    // round-0 weights are unpacked; read step s + 1's round-1 fragments.
-    // Reads and unpacking run a round ahead of the MFMAs that use them, and
-    // the barrier falls between two rounds.  A group's constants are set
-    // after the barrier of the step before its first step.
-    issue_sm(0);
-#pragma unroll
-    for (int s = 0; s < kStages - 2; ++s)
-#pragma unroll
-        for (int p = 0; p < 5; ++p) issue_piece(s, p);
-    issue_piece(kStages - 2, 0);
-    issue_piece(kStages - 2, 1);
-    issue_piece(kStages - 2, 4);
-    wait_vm_barrier<4 * (kStages - 3)>();
-    f16x8 bvA[4], bvB[4], avA[2], avB[2];
-    int2_t wq[2];
+    // Each round's fragments and weights are read and unpacked during the
+    // round before; B_s falls between rounds 2 and 3, and step s + 1's
+    // first operands are read after it, during round 3.
+    wait_vm_barrier<63>();  // B_init (consumers issue no loads: no wait)
+    f16x8 bv0[4], bv1[4], av0[2], av1[2];
+    int4_t wq[2];
     read_wts(0, wq);
-    read_frags(0, 0, bvA);
-    read_frags(0, 1, bvB);
-    group_consts(0);
-    unpack(0, wq, avA);
+    consts(0);
+    read_frags(0, 0, bv0);
+    unpack(0, wq, av0);
 #pragma unroll 1
     for (int s = 0; s < S; ++s) {
-        // round 0, with part 1 of step s + kStages - 2
-        mfmas(avA, bvA, s + kStages - 2, 2, 3, -1);
-        unpack(1, wq, avB);
-        wait_vm_barrier<4 * (kStages - 3)>();
-        if ((s & 3) == 0) issue_sm((s >> 2) + 1);
-        if (kG32)
-            group_consts(s + 1);  // (s + 1 = S reads a stage's stale pairs, unused)
-        else if (((s + 1) & 3) == 0 && s + 1 < S)
-            group_consts((s + 1) >> 2);
-        read_wts(s + 1, wq);
-        read_frags(s + 1, 0, bvA);
-        // round 1, with part 0 of step s + kStages - 1
-        mfmas(avB, bvB, s + kStages - 1, 0, 1, 4);
-        unpack(0, wq, avA);
-        read_frags(s + 1, 1, bvB);
+        read_frags(s, 1, bv1);
+        unpack(1, wq, av1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(av0, bv0);                       // round 0
+        read_frags(s, 2, bv0);
+        unpack(2, wq, av0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(av1, bv1);                       // round 1
+        read_frags(s, 3, bv1);
+        unpack(3, wq, av1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(av0, bv0);                       // round 2
+        wait_vm_barrier<63>();                 // B_s: step s + 1 in LDS
+        int4_t wqn[2];
+        read_wts(s + 1, wqn);
+        if (kG32 || ((s + 1) & 3) == 0) consts(s + 1);
+        read_frags(s + 1, 0, bv0);
+        unpack(0, wqn, av0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(av1, bv1);                       // round 3
+        wq[0] = wqn[0];
+        wq[1] = wqn[1];
     }
-    // the loads past the last step are still in flight into the stages
-    wait_vm_barrier<0>();
 
-    // ---- add the two K halves: wave wk keeps weight tile j = wk and hands
-    // the other tile's sums to its partner (wave ^ 4) through LDS; the tile
-    // indices stay compile-time (a runtime index would put acc in memory) ----
-    float16_t fin[4];
-    auto exchange = [&](auto jc) {
-        constexpr int jk = decltype(jc)::value, jo = 1 - jk;
-        float4 *mine = reinterpret_cast<float4 *>(lds) + wave * 1024;
-        const float4 *theirs = reinterpret_cast<const float4 *>(lds) + (wave ^ 4) * 1024;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                mine[(i * 4 + q) * 64 + lane] =
-                    make_float4(acc[jo][i][4 * q], acc[jo][i][4 * q + 1], acc[jo][i][4 * q + 2], acc[jo][i][4 * q + 3]);
-        __syncthreads();
+    for (int j = 0; j < 2; ++j) {
+        const int nl = wn * 64 + 32 * j;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            fin[i] = acc[jk][i];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 o = theirs[(i * 4 + q) * 64 + lane];
-                fin[i][4 * q] += o.x;
-                fin[i][4 * q + 1] += o.y;
-                fin[i][4 * q + 2] += o.z;
-                fin[i][4 * q + 3] += o.w;
-            }
-        }
-    };
-    if (wk == 0)
-        exchange(IC<0>{});
-    else
-        exchange(IC<1>{});
-
-    // ---- epilogue: lane holds activation row m and weight rows 8 r4 + 4 h + (0..3) ----
-    const int nl = wn * 64 + 32 * wk;  // first weight row of this wave's MFMA tile in the tile
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 128 + 32 * i + l32;
-        const float fi = m < M ? 1.0f / fs[m] : 0.0f;  // exact: fs is a power of two
-        const float16_t &a = fin[i];
-        float v[16];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const float4 sc = *reinterpret_cast<const float4 *>(sScale + nl + 8 * r4 + 4 * h);
-            v[4 * r4] = a[4 * r4] * fi * sc.x;
-            v[4 * r4 + 1] = a[4 * r4 + 1] * fi * sc.y;
-            v[4 * r4 + 2] = a[4 * r4 + 2] * fi * sc.z;
-            v[4 * r4 + 3] = a[4 * r4 + 3] * fi * sc.w;
-        }
-        if (kMode == kFOutQ8) {
-            // the MFMA tile's 32 weight rows are one Q8_1 block along n for
-            // row m: 16 values here and 16 in lane ^ 32 (N is a multiple of
-            // 32, so a block lies wholly inside or outside [0, N))
-            const int nb = n0 + nl;
-            float amax = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
-            const uint16_t d16 = q8_1_scale(amax);
-            const float df = f16_bits_to_f32(d16);
-            int sum = 0;
-            uint32_t packed[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                packed[q] = 0;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int c = q8_1_code(v[4 * q + r], df);
-                    sum += c;
-                    packed[q] |= ((uint32_t)c & 0xFFu) << (8 * r);
-                }
-            }
-            sum += __shfl_xor(sum, 32);
-            if (m < M && nb < N) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<uint32_t *>(qo + (int64_t)m * ldy + nb + 8 * q + 4 * h) = packed[q];
-                if (h == 0) dso[(int64_t)m * (ldy / kBlock) + nb / kBlock] = q8_1_ds(d16, df, sum);
-            }
-        } else if (m < M) {
+            const int m = m0 + wm * 128 + 32 * i + l32;
+            const float fi = m < M ? 1.0f / fs[m] : 0.0f;
+            const float16_t &a = acc[j][i];
+            float v[16];
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int n = n0 + nl + 8 * r4 + 4 * h;
-                float *dst = y + (int64_t)m * ldy + n;
-                if (vec_store && n + 3 < N) {
-                    *reinterpret_cast<float4 *>(dst) = make_float4(v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]);
-                } else {
+                const float4 sc = *reinterpret_cast<const float4 *>(sScale + nl + 8 * r4 + 4 * h);
+                v[4 * r4] = a[4 * r4] * fi * sc.x;
+                v[4 * r4 + 1] = a[4 * r4 + 1] * fi * sc.y;
+                v[4 * r4 + 2] = a[4 * r4 + 2] * fi * sc.z;
+                v[4 * r4 + 3] = a[4 * r4 + 3] * fi * sc.w;
+            }
+            if (kMode == kFOutQ8) {
+                const int nb = n0 + nl;
+                float amax = 0.0f;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        if (n + c < N) dst[c] = v[4 * r4 + c];
+                for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                const uint16_t d16 = q8_1_scale(amax);
+                const float df = f16_bits_to_f32(d16);
+                int sum = 0;
+                uint32_t packed[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    packed[q] = 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int c = q8_1_code(v[4 * q + r], df);
+                        sum += c;
+                        packed[q] |= ((uint32_t)c & 0xFFu) << (8 * r);
+                    }
+                }
+                sum += __shfl_xor(sum, 32);
+                if (m < M && nb < N) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint32_t *>(qo + (int64_t)m * ldy + nb + 8 * q + 4 * h) = packed[q];
+                    if (h == 0) dso[(int64_t)m * (ldy / kBlock) + nb / kBlock] = q8_1_ds(d16, df, sum);
+                }
+            } else if (m < M) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int n = n0 + nl + 8 * r4 + 4 * h;
+                    float *dst = y + (int64_t)m * ldy + n;
+                    if (vec_store && n + 3 < N) {
+                        *reinterpret_cast<float4 *>(dst) =
+                            make_float4(v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            if (n + c < N) dst[c] = v[4 * r4 + c];
+                    }
                 }
             }
         }
@@ -612,16 +525,13 @@ hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const ui
                 float *y0 = y + m0 * N + n0;
                 const int vec_store = (N % 4 == 0) && (nn % 4 == 0) &&
                                       ((reinterpret_cast<uintptr_t>(y0) & 15) == 0);
-                if (g32)
-                    hipLaunchKernelGGL((k_mmqf<kFOutY, true>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream,
-                                       img, img_bytes, fs, qs + n0 * (K / 2), sm32 + n0 * P, y0, (int8_t *)nullptr,
-                                       (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, N, vec_store);
-                else
-                    hipLaunchKernelGGL(k_mmqf<kFOutY>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, img,
-                                       img_bytes, fs, qs + n0 * (K / 2), sm32 + n0 * P, y0, (int8_t *)nullptr,
-                                       (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, N, vec_store);
+                auto kern = g32 ? k_mmqf<kFOutY, true> : k_mmqf<kFOutY, false>;
+                hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, img, img_bytes, fs,
+                                   qs + n0 * (K / 2), sm32 + n0 * P, y0, (int8_t *)nullptr, (uint32_t *)nullptr,
+                                   (int)mm, (int)nn, K, tiles_m, N, vec_store);
             } else {
-                hipLaunchKernelGGL(k_mmqf<kFOutQ8>, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, img, img_bytes, fs,
+                hipLaunchKernelGGL((k_mmqf<kFOutQ8, false>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream,
+                                   img, img_bytes, fs,
                                    qs + n0 * (K / 2), sm32 + n0 * P, (float *)nullptr, qo + m0 * N + n0,
                                    dso32 + m0 * (N / kBlock) + n0 / kBlock, (int)mm, (int)nn, K, tiles_m, N, 0);
             }
