@@ -374,8 +374,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     };
 
     // Each round's fragments and weights are read and unpacked during the
-    // round before; B_s falls between rounds 2 and 3, and step s + 1's
-    // first operands are read after it, during round 3.
+    // round before: one scheduling region holds a round's 8 MFMAs and the
+    // next round's LDS reads and unpack, interleaved one MFMA, one read and
+    // three VALU ops at a time so the VALU runs in the MFMAs' shadow.  B_s
+    // falls between rounds 2 and 3, and step s + 1's first operands are read
+    // after it, during round 3.
+    auto interleave = [&]() {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+        }
+    };
     wait_vm_barrier<63>();  // B_init (consumers issue no loads: no wait)
     f16x8 bv0[4], bv1[4], av0[2], av1[2];
     int4_t wq[2];
@@ -385,26 +396,30 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     unpack(0, wq, av0);
 #pragma unroll 1
     for (int s = 0; s < S; ++s) {
-        read_frags(s, 1, bv1);
-        unpack(1, wq, av1);
         __builtin_amdgcn_sched_barrier(0);
         mfmas(av0, bv0);                       // round 0
-        read_frags(s, 2, bv0);
-        unpack(2, wq, av0);
+        read_frags(s, 1, bv1);
+        unpack(1, wq, av1);
+        interleave();
         __builtin_amdgcn_sched_barrier(0);
         mfmas(av1, bv1);                       // round 1
-        read_frags(s, 3, bv1);
-        unpack(3, wq, av1);
+        read_frags(s, 2, bv0);
+        unpack(2, wq, av0);
+        interleave();
         __builtin_amdgcn_sched_barrier(0);
         mfmas(av0, bv0);                       // round 2
+        read_frags(s, 3, bv1);
+        unpack(3, wq, av1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
         wait_vm_barrier<63>();                 // B_s: step s + 1 in LDS
         int4_t wqn[2];
         read_wts(s + 1, wqn);
         if (kG32 || ((s + 1) & 3) == 0) consts(s + 1);
+        mfmas(av1, bv1);                       // round 3
         read_frags(s + 1, 0, bv0);
         unpack(0, wqn, av0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(av1, bv1);                       // round 3
+        interleave();
         wq[0] = wqn[0];
         wq[1] = wqn[1];
     }
