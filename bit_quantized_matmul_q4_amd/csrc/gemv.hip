@@ -615,8 +615,8 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
     const int nunits = R > gw ? (R - gw + GW - 1) / GW : 0;
     const int nitems = nunits * gc;
     const uint32_t rowbytes = K / 2;
-    float *dst = out + (int64_t)split * M * ldo;  // partials: [split][M][ldo]
-    asm volatile("" : "+s"(dst));  // its arguments with the others, not in a dependent load later
+    // partials [split][M][ldo] (or y itself): the host keeps every offset below 2^31
+    const rsrc_t r_out = make_rsrc(out + (int64_t)split * M * ldo, (uint32_t)(((int64_t)(M - 1) * ldo + N) * 4));
     uint8_t *tile = xl + arm_b_x_lds_bytes(gc, GS) + wave * arm_b_tile_bytes(GS);
     uint32_t *tile_sm = reinterpret_cast<uint32_t *>(tile + kBRows * kBTileRow);  // GS 32: [row][run]
 
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
                 if (cu < nunits && n < N) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (4 * kg + e < M) dst[(int64_t)(4 * kg + e) * ldo + n] = yacc[e];
+                        if (4 * kg + e < M) buf_store4(r_out, ((uint32_t)(4 * kg + e) * (uint32_t)ldo + (uint32_t)n) * 4u, yacc[e]);
                 }
                 yacc = float4_t{0.f, 0.f, 0.f, 0.f};
                 cg = 0;
@@ -834,6 +834,8 @@ hipError_t launch_arm_b(const float *x, int M, const uint8_t *qs, const uint16_t
     float *out = c.nsplit > 1 ? static_cast<float *>(workspace) : y;
     const int64_t ldo = c.nsplit > 1 ? N : ldy;
     const uint32_t *sm32 = reinterpret_cast<const uint32_t *>(sm);
+    // the kernel addresses its output through one descriptor with 32-bit offsets
+    if (((int64_t)(M - 1) * ldo + N) * 4 > kMaxBufferBytes) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(wps * c.nsplit)), block(kBThreads);
     if (GS == 32) {
         hipLaunchKernelGGL((k_gemv_mfma<kBDepth, false, 32>), grid, block, lds, stream, x, qs, sm32, out, ldo,

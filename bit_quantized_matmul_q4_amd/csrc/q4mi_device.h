@@ -99,6 +99,15 @@ __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off)
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
+// Raw buffer store; bytes outside the descriptor are dropped.  A buffer (not
+// flat) store keeps the compiler's wait analysis exact: flat accesses count
+// against both the vector-memory and the LDS counters, after which every
+// later load or LDS read is awaited down to zero outstanding.
+__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+}
+
 // Streaming variants for data read exactly once (the GEMV weights): the
 // non-temporal cache policy (gfx940-family NT bit) keeps them from displacing
 // reused lines; on MI355X it also lifts the streamed read rate by about 8 %.
