@@ -468,7 +468,7 @@ constexpr int kBRows = 16;                      // weight rows per unit (one MFM
 constexpr int kBWaves = 8;                      // waves per workgroup
 constexpr int kBThreads = kBWaves * kWave;
 constexpr int kBGroupLds = 8 * 4 * kBRows * 16; // A image of one group: [step 8][kg 4][m 16] x 16 B
-constexpr int kBDepth = 8;                      // (unit, group) items in flight per wave
+constexpr int kBDepth = 4;                      // (unit, group) items in flight per wave
 constexpr int kBTargetUnits = 256 * kBWaves;    // units wanted before K is split further
 constexpr int kBTileRow = 9 * 16;               // weight tile row: 8 chunks of 16 B + 16 B pad
 
