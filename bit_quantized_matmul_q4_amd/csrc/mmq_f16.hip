@@ -84,6 +84,17 @@ __device__ __forceinline__ int xcd_tile_f(int pid, int ntiles)
 // F[r] for rows r < rows: 2^(8 - e) with e the binary exponent of the row's
 // largest block scale (d = f * 2^e, f in [0.5, 1)), so 127 * d * F < 2^15;
 // 1 for rows past M, all-zero rows and non-finite scales.  One wave per row.
+__device__ __forceinline__ float row_factor(uint32_t dm)
+{
+    float f = 1.0f;
+    if (dm != 0 && dm < 0x7C00u) {
+        int e;
+        frexpf(f16_bits_to_f32(dm), &e);
+        f = ldexpf(1.0f, 8 - e);
+    }
+    return f;
+}
+
 __global__ __launch_bounds__(256) void k_mmqf_rowscale(const uint32_t *__restrict__ ds, int M, int B, int rows,
                                                        float *__restrict__ fs)
 {
@@ -96,15 +107,7 @@ __global__ __launch_bounds__(256) void k_mmqf_rowscale(const uint32_t *__restric
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) dm = max(dm, (uint32_t)__shfl_xor((int)dm, o));
-    if (lane == 0) {
-        float f = 1.0f;
-        if (dm != 0 && dm < 0x7C00u) {
-            int e;
-            frexpf(f16_bits_to_f32(dm), &e);
-            f = ldexpf(1.0f, 8 - e);
-        }
-        fs[row] = f;
-    }
+    if (lane == 0) fs[row] = row_factor(dm);
 }
 
 // The fp16 activation image of one (256-row tile mt, K step s): thread r
@@ -112,9 +115,14 @@ __global__ __launch_bounds__(256) void k_mmqf_rowscale(const uint32_t *__restric
 // step (t = 0..3 MFMA of the step, h = Q8_1 block of the step) holds
 // x'[k] for k = 64 s + 32 h + {4t, 4t+2, 16+4t, 18+4t, 4t+1, 4t+3, 17+4t, 19+4t}:
 // the order in which the GEMM unpacks one 32-bit word of packed weights.
+// kRowScale: each thread also finds its row's factor itself (all the row's
+// block scales, loaded a round of 8 vectors at a time) and the step-0
+// workgroups store it for the GEMM's epilogue, in place of k_mmqf_rowscale;
+// taken when those repeated reads stay small (short K, few row tiles).
+template <bool kRowScale>
 __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restrict__ qa,
                                                           const uint32_t *__restrict__ ds,
-                                                          const float *__restrict__ fs, int M, int K,
+                                                          float *__restrict__ fs, int M, int K,
                                                           uint4 *__restrict__ img)
 {
     const int s = blockIdx.x, mt = blockIdx.y, r = threadIdx.x;
@@ -130,7 +138,23 @@ __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restri
         const uint32_t *dp = ds + (int64_t)m * (K / kBlock) + 2 * s;
         dw[0] = dp[0];
         dw[1] = dp[1];
-        F = fs[m];
+        if (kRowScale) {
+            const int B4 = K / kBlock / 4;  // 16-byte vectors of the row's (d, s) pairs
+            const uint4 *p = reinterpret_cast<const uint4 *>(ds + (int64_t)m * (K / kBlock));
+            uint32_t dm = 0;
+            for (int b0 = 0; b0 < B4; b0 += 8) {
+                uint4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = b0 + u < B4 ? p[b0 + u] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    dm = max(dm, max(max(v[u].x & 0x7FFFu, v[u].y & 0x7FFFu), max(v[u].z & 0x7FFFu, v[u].w & 0x7FFFu)));
+            }
+            F = row_factor(dm);
+            if (s == 0) fs[m] = F;
+        } else {
+            F = fs[m];
+        }
     }
     uint4 *dst = img + ((int64_t)mt * S + s) * kStepVecs + r;
 #pragma unroll
@@ -489,6 +513,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
 
 int64_t round_up(int64_t v, int64_t u) { return (v + u - 1) / u * u; }
 
+constexpr int64_t kFusedScaleBytes = (int64_t)8 << 20;
+
 // activation rows per launch: the whole (padded) M, or as many 256-row tiles
 // as keep the image within kImageMaxBytes (at least one tile)
 int64_t chunk_rows(int64_t M, int64_t K)
@@ -528,10 +554,19 @@ hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const ui
         const int64_t mp = round_up(mm, kFm);
         const int tiles_m = (int)(mp / kFm);
         const uint32_t img_bytes = (uint32_t)(mp * K * 2);  // <= kImageMaxBytes (or one tile's)
-        hipLaunchKernelGGL(k_mmqf_rowscale, dim3((unsigned)(mp / 4)), dim3(256), 0, stream, ds32 + m0 * B,
-                           (int)mm, B, (int)mp, fs);
-        hipLaunchKernelGGL(k_mmqf_image, dim3((unsigned)S, (unsigned)tiles_m), dim3(kFThreads), 0, stream,
-                           qa + m0 * K, ds32 + m0 * B, fs, (int)mm, K, img);
+        // the image workgroups find the row factors themselves while the
+        // row-scale reads they repeat (each step re-reads its rows' scales)
+        // stay within kFusedScaleBytes and the scales allow 16-byte loads;
+        // otherwise a separate pass
+        if (mp * S * B * 4 <= kFusedScaleBytes && (reinterpret_cast<uintptr_t>(ds) & 15) == 0) {
+            hipLaunchKernelGGL(k_mmqf_image<true>, dim3((unsigned)S, (unsigned)tiles_m), dim3(kFThreads), 0,
+                               stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm, K, img);
+        } else {
+            hipLaunchKernelGGL(k_mmqf_rowscale, dim3((unsigned)(mp / 4)), dim3(256), 0, stream, ds32 + m0 * B,
+                               (int)mm, B, (int)mp, fs);
+            hipLaunchKernelGGL(k_mmqf_image<false>, dim3((unsigned)S, (unsigned)tiles_m), dim3(kFThreads), 0,
+                               stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm, K, img);
+        }
         for (int64_t n0 = 0; n0 < N; n0 += n_max) {
             const int64_t nn = N - n0 < n_max ? N - n0 : n_max;
             const int64_t tiles = (int64_t)tiles_m * ((nn + kFn - 1) / kFn);
