@@ -192,7 +192,7 @@ def cpu_baseline(wl):
     return out
 
 
-def tiny_m_sweep(q4, wl, dev, stream, reps=6):
+def tiny_m_sweep(q4, wl, dev, stream, reps=12):
     """GEMV at M = 1..16 on the lm_head shape (K=4096, N=151936), outside the
     timed step: two weight copies (2 x 321 MB) alternate so the Infinity Cache
     cannot serve them; median of per-launch HIP-event times."""
@@ -211,8 +211,8 @@ def tiny_m_sweep(q4, wl, dev, stream, reps=6):
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
         ws_n = q4.q4_gemv_workspace_bytes(M, N, K)
         ws = torch.empty((max(ws_n, 1),), dtype=torch.uint8, device=dev)
-        for i in range(2):
-            q4.q4_gemv(x, *copies[i], y=y, workspace=ws)
+        for i in range(6):  # three warm calls per weight copy
+            q4.q4_gemv(x, *copies[i % 2], y=y, workspace=ws)
         times = []
         for r in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -377,8 +377,9 @@ def group32_figures(q4, wl, dev, stream):
     group-32 pairs: N*K/2 + N*K/32*4."""
     import torch
 
-    def timed(fn, reps=6):
-        fn()
+    def timed(fn, reps=12):
+        for r in range(4):  # warm calls, both weight copies
+            fn(r)
         ts = []
         for r in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
