@@ -24,6 +24,12 @@
 //     N(0, 0.02) / N(0, 1) workloads, against a 1e-6 budget).
 //   * Per group: y += scale * (f * dot + c) + minimum * X, where f = 2^(24+e)
 //     undoes the scalings and X is the exact fp32 sum of the activations.
+//     The running sums carry y * 2^-kYShift (f, c and X are stored that
+//     much smaller) and the stores multiply by 2^kYShift, so f stays finite
+//     for every finite activation (f = 2^(24+e) alone overflows once a chunk
+//     reaches 2^118); the exponent e is clamped at -127 so 2^-e stays finite
+//     for the smallest chunks (all-zero up to fp32 subnormals).  Powers of
+//     two change no rounding in the normal range.
 //   * Fixed reduction orders, no atomics: reruns are bit-identical.
 //
 // Arm A, "dot2" (M = 1, VALU): the workgroup converts x once into LDS; G lanes
@@ -64,13 +70,23 @@ __device__ __forceinline__ void widen(uint32_t w, uint32_t (&p)[4])
     p[3] = w8 & 0x00F000F0u;
 }
 
-// power-of-two exponent sc with amax * 2^-sc in [2^14, 2^15)
+// power-of-two exponent sc with amax * 2^-sc in [2^14, 2^15), but at least
+// -127 so that 2^-sc is finite: a chunk below 2^-113 (fp32 subnormals
+// included) is scaled by 2^127 and still lands in fp16's normal range down to
+// about 2^-141.  At most 2^128 / 2^14: sc <= 113.
+constexpr int kMinChunkExp = -127;
 __device__ __forceinline__ int chunk_exp(float amax)
 {
     int e = 0;
     if (amax > 0.0f) (void)frexpf(amax, &e);
-    return e - 15;
+    return max(e - 15, kMinChunkExp);
 }
+
+// Partial sums are carried at 2^-kYShift of their value: f = 2^(24-kYShift+sc)
+// <= 2^127, X and c (computed from the scaled activations) below 2^127 for
+// any finite x; the stored outputs are multiplied back by 2^kYShift.
+constexpr int kYShift = 10;
+__device__ __forceinline__ float unshift(float v) { return v * (float)(1 << kYShift); }
 
 // ------------------------------------------------------------------ arm A --
 
@@ -123,14 +139,17 @@ __device__ __forceinline__ void convert_x_items(int nitems, int nthr, int base, 
         const float4 a = v.a[it], b = v.b[it];
         float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                            fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-        float sum = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
         // the chunk's four dwords sit in one lane quad: quad-swap DPP, not LDS
         amax = fmaxf(amax, dpp_f32<kDppQuadSwap1>(amax));
         amax = fmaxf(amax, dpp_f32<kDppQuadSwap2>(amax));
-        sum += dpp_f32<kDppQuadSwap1>(sum);
-        sum += dpp_f32<kDppQuadSwap2>(sum);
         const int sc = chunk_exp(amax);
         const float ls = ldexpf(1.0f, -sc), hs = ldexpf(1.0f, -sc - 4);
+        // the sum of x, taken on the scaled values (no overflow; the same
+        // roundings as on x itself), then brought to 2^-kYShift of its value
+        float sum = ((a.x * ls + a.y * ls) + (a.z * ls + a.w * ls)) +
+                    ((b.x * ls + b.y * ls) + (b.z * ls + b.w * ls));
+        sum += dpp_f32<kDppQuadSwap1>(sum);
+        sum += dpp_f32<kDppQuadSwap2>(sum);
         // pairs of dword i: (4i, 4i+2) (16+4i, 16+4i+2) (4i+1, 4i+3) (16+4i+1, 16+4i+3)
         const float w[8] = {a.x * ls, a.z * ls, b.x * hs, b.z * hs, a.y * ls, a.w * ls, b.y * hs, b.w * hs};
         uint32_t hw[4];
@@ -142,7 +161,7 @@ __device__ __forceinline__ void convert_x_items(int nitems, int nthr, int base, 
             if (p & 1) dh += r; else dl += r;
             hw[p] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
         }
-        float delta = ldexpf(dl, sc) + ldexpf(dh, sc + 4);
+        float delta = ldexpf(dl, sc - kYShift) + ldexpf(dh, sc + 4 - kYShift);
         delta += dpp_f32<kDppQuadSwap1>(delta);
         delta += dpp_f32<kDppQuadSwap2>(delta);
         if (idx < nitems) {
@@ -150,7 +169,8 @@ __device__ __forceinline__ void convert_x_items(int nitems, int nthr, int base, 
             const int i = idx & 3;
             *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
             if (i == 0)
-                *reinterpret_cast<float4 *>(dst + 64) = make_float4(ldexpf(1.0f, 24 + sc), sum, 7.5f * delta, 0.0f);
+                *reinterpret_cast<float4 *>(dst + 64) = make_float4(
+                    ldexpf(1.0f, 24 - kYShift + sc), ldexpf(sum, sc - kYShift), 7.5f * delta, 0.0f);
         }
     }
 }
@@ -293,7 +313,7 @@ __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
                 p[u][r] = 0.0f;
                 const int n = b * RB + u * RPW + rq;
                 if (S == 1) {
-                    if (j == 0 && n < N && r < M) y[(int64_t)r * ldy + n] = v;
+                    if (j == 0 && n < N && r < M) y[(int64_t)r * ldy + n] = unshift(v);
                 } else if (j == 0) {
                     red[((bi * S + s) * RB + u * RPW + rq) * MR + r] = v;
                 }
@@ -308,7 +328,7 @@ __global__ __launch_bounds__(1024) void k_gemv_dot2(const float *__restrict__ x,
                         float v = 0.0f;
                         for (int k = 0; k < S; ++k) v += red[((bi * S + k) * RB + u * RPW + rq) * MR + r];
                         const int n = b * RB + u * RPW + rq;
-                        if (n < N && r < M) y[(int64_t)r * ldy + n] = v;
+                        if (n < N && r < M) y[(int64_t)r * ldy + n] = unshift(v);
                     }
             }
             __syncthreads();
@@ -535,14 +555,17 @@ __device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupI
         const float4 a = v.a[it], b = v.b[it];
         float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                            fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-        float sum = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
         // the power-of-two scale is per group of 256; the sums per (scale, minimum) group
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-#pragma unroll
-        for (int o = 1; o < GS / 8; o <<= 1) sum += __shfl_xor(sum, o);
         const int sc = chunk_exp(amax);
         const float ls = ldexpf(1.0f, -sc), hs = ldexpf(1.0f, -sc - 4);
+        // sum of x on the scaled values (as in arm A)
+        float sum = ((a.x * ls + a.y * ls) + (a.z * ls + a.w * ls)) +
+                    ((b.x * ls + b.y * ls) + (b.z * ls + b.w * ls));
+#pragma unroll
+        for (int o = 1; o < GS / 8; o <<= 1) sum += __shfl_xor(sum, o);
+        sum = ldexpf(sum, sc - kYShift);
         // slot order of one widened dword: (4t, 4t+2) (16+4t, 16+4t+2) (4t+1, 4t+3) (16+4t+1, 16+4t+3)
         const float w[8] = {a.x * ls, a.z * ls, b.x * hs, b.z * hs, a.y * ls, a.w * ls, b.y * hs, b.w * hs};
         uint32_t hw[4];
@@ -554,7 +577,7 @@ __device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupI
             if (p & 1) dh += r; else dl += r;
             hw[p] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
         }
-        float delta = ldexpf(dl, sc) + ldexpf(dh, sc + 4);
+        float delta = ldexpf(dl, sc - kYShift) + ldexpf(dh, sc + 4 - kYShift);
 #pragma unroll
         for (int o = 1; o < GS / 8; o <<= 1) delta += __shfl_xor(delta, o);
         if (gl < gc) {
@@ -564,7 +587,7 @@ __device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupI
             *reinterpret_cast<uint4 *>(lds + (size_t)gl * kBGroupLds + ((d * 4 + kg) * kBRows + m) * 16) =
                 make_uint4(hw[0], hw[1], hw[2], hw[3]);
             float *fg = fac + gl * F;
-            if (sub == 0) fg[m] = ldexpf(1.0f, 24 + sc);
+            if (sub == 0) fg[m] = ldexpf(1.0f, 24 - kYShift + sc);
             if (GS == 32 && t == 0) {
                 fg[kBRows + c * kBRows + m] = sum;
                 fg[kBRows + 8 * kBRows + c * kBRows + m] = 7.5f * delta;
@@ -770,7 +793,8 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
                 if (cu < nunits && n < N) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (4 * kg + e < M) buf_store4(r_out, ((uint32_t)(4 * kg + e) * (uint32_t)ldo + (uint32_t)n) * 4u, yacc[e]);
+                        if (4 * kg + e < M)
+                            buf_store4(r_out, ((uint32_t)(4 * kg + e) * (uint32_t)ldo + (uint32_t)n) * 4u, unshift(yacc[e]));
                 }
                 yacc = float4_t{0.f, 0.f, 0.f, 0.f};
                 cg = 0;
@@ -818,11 +842,10 @@ MfmaCfg choose_mfma(int64_t N, int K, int GS)
 }
 
 template <int GS>
-hipError_t launch_arm_b(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
-                        int64_t ldy, int K, float *y, void *workspace, const DeviceInfo &dev,
+hipError_t launch_arm_b(const MfmaCfg &c, const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                        int64_t ldy, int K, float *y, void *workspace, size_t ws_bytes, const DeviceInfo &dev,
                         hipStream_t stream)
 {
-    const MfmaCfg c = choose_mfma(N, K, GS);
     const size_t lds = arm_b_lds_bytes(c.gps, GS);
     if (lds > (size_t)dev.lds_bytes) return hipErrorInvalidConfiguration;
     const int64_t R = (N + kBRows - 1) / kBRows;
@@ -830,11 +853,16 @@ hipError_t launch_arm_b(const float *x, int M, const uint8_t *qs, const uint16_t
     int64_t wps = dev.num_cus / c.nsplit;
     if (wps < 1) wps = 1;
     if (wps > (R + kBWaves - 1) / kBWaves) wps = (R + kBWaves - 1) / kBWaves;
-    // split-K partials are dense [nsplit][M][N]; otherwise y is written directly
+    // split-K partials are dense [nsplit][M][N] in the workspace (which must
+    // hold them: the plan was made for the whole matrix, this is one row range
+    // of it); otherwise y is written directly
+    if (c.nsplit > 1 && (workspace == nullptr || (size_t)c.nsplit * M * N * sizeof(float) > ws_bytes))
+        return hipErrorInvalidValue;
     float *out = c.nsplit > 1 ? static_cast<float *>(workspace) : y;
     const int64_t ldo = c.nsplit > 1 ? N : ldy;
     const uint32_t *sm32 = reinterpret_cast<const uint32_t *>(sm);
-    // the kernel addresses its output through one descriptor with 32-bit offsets
+    // the kernel addresses its output through one descriptor with 32-bit
+    // offsets (the C ABI rejects shapes beyond it, so this does not trigger)
     if (((int64_t)(M - 1) * ldo + N) * 4 > kMaxBufferBytes) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(wps * c.nsplit)), block(kBThreads);
     if (GS == 32) {
@@ -858,11 +886,6 @@ hipError_t launch_arm_b(const float *x, int M, const uint8_t *qs, const uint16_t
     return hipGetLastError();
 }
 
-template <int GS>
-hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
-                            int64_t ldy, int K, float *y, void *workspace, const DeviceInfo &dev,
-                            hipStream_t stream);
-
 }  // namespace
 
 // Largest K whose activation image arm A holds in LDS (80 B per 32 of K and
@@ -878,8 +901,7 @@ constexpr int kArmAMaxK4 = 15360;
 // rows only below 65536 weight rows: there the matrix-core arm's fixed costs
 // (activation image per workgroup, K split with a second pass) dominate
 // (4096 x 4096 at M = 4: 9.8 vs 20.6 us), while on the lm_head widths four
-// rows make arm A VALU-bound (88 vs 72 us at K = 4096).  A function of the
-// shape only, so the workspace query agrees with the launch.
+// rows make arm A VALU-bound (88 vs 72 us at K = 4096).
 constexpr int64_t kArmA4MaxN = 65536;
 int arm_a_rows(int64_t M, int64_t N, int64_t K)
 {
@@ -889,21 +911,55 @@ int arm_a_rows(int64_t M, int64_t N, int64_t K)
     return 0;
 }
 
+// Weight rows one launch addresses: one descriptor reaches < 2 GiB of qs,
+// so taller matrices run as row ranges of at most this many rows.
+int64_t gemv_range_rows(int64_t K) { return ((kMaxBufferBytes - 1) / (K / 2)) / 64 * 64; }
+
+// The plan of an M x N x K call, a function of the whole shape only: every
+// row range of a tall matrix runs the same arm with the same K split, and the
+// workspace query, the argument check and the launch all agree.
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group)
+{
+    GemvPlan p{};
+    p.MR = arm_a_rows(M, N, K);
+    if (p.MR == 0) {
+        const MfmaCfg c = choose_mfma(N, (int)K, group);
+        p.nsplit = c.nsplit;
+        p.gps = c.gps;
+    } else {
+        p.nsplit = 1;
+        p.gps = 0;
+    }
+    return p;
+}
+
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group)
 {
-    if (M < 1 || arm_a_rows(M, N, K) != 0) return 0;
-    const MfmaCfg c = choose_mfma(N, (int)K, group);
-    return c.nsplit > 1 ? (size_t)c.nsplit * M * N * sizeof(float) : 0;
+    if (M < 1 || N < 1 || K < kGroup) return 0;
+    const GemvPlan p = plan_gemv(M, N, K, group);
+    if (p.MR != 0 || p.nsplit == 1) return 0;
+    // partials [nsplit][M][rows of the largest range]; the ranges run one
+    // after another on the stream and reuse the same bytes
+    const int64_t rows = N < gemv_range_rows(K) ? N : gemv_range_rows(K);
+    return (size_t)p.nsplit * (size_t)M * (size_t)rows * sizeof(float);
+}
+
+bool gemv_shape_supported(int64_t M, int64_t N, int64_t K, int group)
+{
+    if (M < 1 || N < 1 || K < kGroup) return true;
+    const GemvPlan p = plan_gemv(M, N, K, group);
+    // the matrix-core arm without a K split writes y through one descriptor
+    return !(p.MR == 0 && p.nsplit == 1 && M * N > kMaxBufferBytes / 4);
 }
 
 namespace {
 
 template <int GS>
-hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
-                            int64_t ldy, int K, float *y, void *workspace, const DeviceInfo &dev,
-                            hipStream_t stream)
+hipError_t launch_gemv_rows(const GemvPlan &p, const float *x, int M, const uint8_t *qs, const uint16_t *sm,
+                            int64_t N, int64_t ldy, int K, float *y, void *workspace, size_t ws_bytes,
+                            const DeviceInfo &dev, hipStream_t stream)
 {
-    const int MR = arm_a_rows(M, N, K);
+    const int MR = p.MR;
     if (MR != 0) {
         const Dot2Cfg c = choose_dot2(N, K, MR, dev);
         if (MR == 1)
@@ -915,25 +971,28 @@ hipError_t launch_gemv_rows(const float *x, int M, const uint8_t *qs, const uint
         return c.G == 16 ? dispatch_dot2<16, GS, 4>(c, x, M, qs, sm, N, ldy, K, y, dev, stream)
                          : dispatch_dot2<8, GS, 4>(c, x, M, qs, sm, N, ldy, K, y, dev, stream);
     }
-    return launch_arm_b<GS>(x, M, qs, sm, N, ldy, K, y, workspace, dev, stream);
+    return launch_arm_b<GS>(MfmaCfg{p.nsplit, p.gps}, x, M, qs, sm, N, ldy, K, y, workspace, ws_bytes, dev,
+                            stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
-                       int K, int group, float *y, void *workspace, const DeviceInfo &dev,
+                       int K, int group, float *y, void *workspace, size_t ws_bytes, const DeviceInfo &dev,
                        hipStream_t stream)
 {
+    const GemvPlan p = plan_gemv(M, N, K, group);
     // one descriptor addresses < 2 GiB of weights: split taller matrices into
     // row ranges (y keeps its row stride N)
-    const int64_t rows_max = ((kMaxBufferBytes - 1) / (K / 2)) / 64 * 64;
+    const int64_t rows_max = gemv_range_rows(K);
     for (int64_t n0 = 0; n0 < N; n0 += rows_max) {
         const int64_t nn = N - n0 < rows_max ? N - n0 : rows_max;
         const uint8_t *qs0 = qs + n0 * (K / 2);
         const uint16_t *sm0 = sm + n0 * (K / group) * 2;
         const hipError_t e =
-            group == 32 ? launch_gemv_rows<32>(x, M, qs0, sm0, nn, N, K, y + n0, workspace, dev, stream)
-                        : launch_gemv_rows<kGroup>(x, M, qs0, sm0, nn, N, K, y + n0, workspace, dev, stream);
+            group == 32
+                ? launch_gemv_rows<32>(p, x, M, qs0, sm0, nn, N, K, y + n0, workspace, ws_bytes, dev, stream)
+                : launch_gemv_rows<kGroup>(p, x, M, qs0, sm0, nn, N, K, y + n0, workspace, ws_bytes, dev, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

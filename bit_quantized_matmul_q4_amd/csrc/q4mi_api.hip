@@ -109,9 +109,16 @@ int q8_1_quantize(const float *x, int64_t M, int64_t K, int8_t *qa, uint16_t *ds
     return launch_status(q4mi::launch_q8_1_quantize(x, M, K, qa, ds, dev->num_cus, (hipStream_t)stream));
 }
 
+// shape rules of q4_gemv / q4_gemv_g32 (pointers aside)
+static bool gemv_shape_ok(int64_t M, int64_t N, int64_t K, int group)
+{
+    return M >= 0 && M <= Q4_GEMV_MAX_M && N >= 0 && N <= Q4_MAX_N && valid_k(K, 256) &&
+           q4mi::gemv_shape_supported(M, N, K, group);
+}
+
 static size_t gemv_ws_common(int64_t M, int64_t N, int64_t K, int group)
 {
-    if (M < 0 || M > Q4_GEMV_MAX_M || N < 0 || N > Q4_MAX_N || !valid_k(K, 256)) return 0;
+    if (!gemv_shape_ok(M, N, K, group)) return 0;
     return q4mi::gemv_workspace_bytes(M, N, K, group);
 }
 
@@ -121,7 +128,7 @@ size_t q4_gemv_g32_workspace_bytes(int64_t M, int64_t N, int64_t K) { return gem
 static int gemv_common(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N,
                        int64_t K, int group, float *y, void *workspace, size_t ws_bytes, void *stream)
 {
-    if (M < 0 || M > Q4_GEMV_MAX_M || N < 0 || N > Q4_MAX_N || !valid_k(K, 256)) return Q4_ERR_ARG;
+    if (!gemv_shape_ok(M, N, K, group)) return Q4_ERR_ARG;
     if (M == 0 || N == 0) return Q4_OK;
     if (!x || !qs || !sm || !y) return Q4_ERR_ARG;
     if (!aligned(x, 16) || !aligned(qs, 16) || !aligned(sm, 4) || !aligned(y, 4)) return Q4_ERR_ALIGN;
@@ -130,8 +137,8 @@ static int gemv_common(const float *x, int64_t M, const uint8_t *qs, const uint1
     if (need > 0 && !aligned(workspace, 16)) return Q4_ERR_ALIGN;
     const DeviceInfo *dev = nullptr;
     if (int rc = current_device(&dev)) return rc;
-    return launch_status(q4mi::launch_gemv(x, (int)M, qs, sm, N, (int)K, group, y, workspace, *dev,
-                                           (hipStream_t)stream));
+    return launch_status(q4mi::launch_gemv(x, (int)M, qs, sm, N, (int)K, group, y, workspace,
+                                           need > 0 ? ws_bytes : 0, *dev, (hipStream_t)stream));
 }
 
 int q4_gemv(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N, int64_t K,

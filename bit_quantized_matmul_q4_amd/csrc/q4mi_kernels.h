@@ -18,10 +18,18 @@ hipError_t launch_q4_pack(const float *W, int64_t N, int64_t K, int group, uint8
 hipError_t launch_q8_1_quantize(const float *x, int64_t M, int64_t K, int8_t *qa, uint16_t *ds,
                                 int num_cus, hipStream_t stream);
 
-// group: the (scale, minimum) group along K, 256 or 32
+// group: the (scale, minimum) group along K, 256 or 32.
+// The GEMV plan depends on the whole shape only: MR activation rows on the
+// VALU arm (0 = matrix-core arm) and, for the matrix-core arm, the K split.
+struct GemvPlan {
+    int MR, nsplit, gps;
+};
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int group);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group);
+// false for shapes whose output the plan cannot address (see q4_gemv)
+bool gemv_shape_supported(int64_t M, int64_t N, int64_t K, int group);
 hipError_t launch_gemv(const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
-                       int K, int group, float *y, void *workspace, const DeviceInfo &dev,
+                       int K, int group, float *y, void *workspace, size_t ws_bytes, const DeviceInfo &dev,
                        hipStream_t stream);
 
 size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);

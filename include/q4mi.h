@@ -127,7 +127,18 @@ size_t q4_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * sum_k x[m][k] * (scale * q + minimum) to max|dy| / max|y| <= 2e-3 and
  * sum(dy^2) / sum(y^2) <= 1e-6 on well-scaled inputs (activations are rounded
  * to fp16 with a power-of-two scale per 32-element chunk inside the kernel).
+ * Every finite x gives finite y unless the exact y itself overflows fp32:
+ * chunks anywhere from fp32 subnormals to the fp32 maximum are scaled into
+ * fp16's range (chunks below 2^-113 by 2^127), and the partial sums are
+ * carried at 2^-10 of their value; rows whose outputs fall below about 1e-37
+ * are accurate to about 2^-130 absolute rather than relatively.
  * Reruns with the same inputs are bit-identical.
+ * Shape limit: when the shape runs on the matrix-core arm without a K split
+ * (M >= 5, or M = 3..4 with N >= 65536 or K > 15360, or M = 2 with
+ * K > 31744, or M = 1 with K > 64512; and N large enough that K is not
+ * split), M * N must not exceed 2^29 (y is addressed through one 2 GiB
+ * buffer descriptor); larger shapes return Q4_ERR_ARG.  Weights beyond
+ * 2 GiB are fine: they run as row ranges of one plan.
  *   x:  device fp32 [M][K], 16-byte aligned.   qs: device u8 [N][K/2],
  *   16-byte aligned.   sm: device u16 [N][K/256][2], 4-byte aligned.
  *   y:  device fp32 [M][N], 4-byte aligned; must not overlap the inputs.
@@ -136,8 +147,8 @@ size_t q4_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   are ignored and on exit are unspecified.  Two calls that run concurrently
  *   must not share a workspace.
  * Errors: Q4_ERR_ARG (M outside 0..16, N < 0, K not a positive multiple of
- * 256, null pointer), Q4_ERR_ALIGN, Q4_ERR_WORKSPACE, Q4_ERR_ARCH,
- * Q4_ERR_DEVICE, Q4_ERR_LAUNCH.
+ * 256, the shape limit above, null pointer), Q4_ERR_ALIGN, Q4_ERR_WORKSPACE,
+ * Q4_ERR_ARCH, Q4_ERR_DEVICE, Q4_ERR_LAUNCH.
  */
 int q4_gemv(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N,
             int64_t K, float *y, void *workspace, size_t ws_bytes, void *stream);

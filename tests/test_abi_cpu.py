@@ -137,3 +137,24 @@ def test_mmq_q8_1_output_argument_checks():
     assert fn(NULL, NULL, 0, NULL, NULL, 64, 256, NULL, NULL, NULL, 0, NULL) == 0
     assert fn(FAKE, FAKE, 4, FAKE, FAKE, 64, 256, NULL, FAKE, NULL, 0, NULL) == ARG
     assert fn(FAKE, FAKE, 4, FAKE, FAKE, 64, 256, FAKE, NULL, NULL, 0, NULL) == ARG
+
+
+def test_gemv_plan_is_made_for_the_whole_shape():
+    # 1048576 x 4096 weights run as two row ranges (1048512 rows and 64); the
+    # plan, and with it the workspace, comes from the whole shape: no K split
+    # at M = 8 (a 64-row matrix on its own would split K)
+    assert q4.q4_gemv_workspace_bytes(8, 1048576, 4096) == 0
+    assert q4.q4_gemv_workspace_bytes(8, 64, 4096) > 0
+    # the K-split partials of the largest row range: nsplit x M x rows
+    ws = q4.q4_gemv_workspace_bytes(8, 300, 2560)
+    assert ws > 0 and ws % (8 * 300 * 4) == 0
+
+
+def test_gemv_output_beyond_one_descriptor_rejected():
+    # the matrix-core arm without a K split addresses y through one 2 GiB
+    # descriptor: M * N <= 2^29
+    L = q4.lib()
+    assert L.q4_gemv(FAKE, 16, FAKE, FAKE, 40000000, 256, FAKE, NULL, 0, NULL) == ARG
+    assert q4.q4_gemv_workspace_bytes(16, 40000000, 256) == 0
+    # one activation row on the VALU arm writes y with 64-bit indexing: allowed
+    assert q4.q4_gemv_workspace_bytes(1, 40000000, 256) == 0

@@ -136,18 +136,15 @@ def test_mmq_g32_parity(q4, orc, M, N, K, outl):
 
 def test_mmq_g32_512(q4, orc):
     c = wl.MMQ_512
-    say("mmq g32 M=512 K=2560 N=9216 (sampled activation rows)")
-    rows = np.unique(np.concatenate([[0, 511], np.random.default_rng(5).choice(512, 62, replace=False)]))
-    mmq_g32_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq g32 512", mrows=rows)
+    say("mmq g32 M=512 K=2560 N=9216 (every output)")
+    mmq_g32_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq g32 512")
 
 
 @pytest.mark.parametrize("idx", [0, 1])
 def test_mmq_g32_2048(q4, orc, idx):
     c = wl.MMQ_2048[idx]
-    say("mmq g32 M=2048 %s (sampled activation rows)" % c["name"])
-    rows = np.unique(np.concatenate([[0, 2047], np.random.default_rng(9 + idx).choice(2048, 30, replace=False)]))
-    mmq_g32_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq g32 2048 " + c["name"],
-                  mrows=rows)
+    say("mmq g32 M=2048 %s (every output)" % c["name"])
+    mmq_g32_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq g32 2048 " + c["name"])
 
 
 def test_mmq_g32_equal_pairs_match_g256(q4, orc):

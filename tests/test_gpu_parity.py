@@ -118,11 +118,11 @@ def test_q8_1_bitexact(q4, orc, M, K, outl):
 
 
 def test_q8_1_beyond_one_descriptor(q4, orc):
-    # 8200 x 65536 activations (2.15 GB of fp32) take two launches, the first
-    # covering 536870880 elements (just under 2 GiB), so the boundary falls
-    # inside row 8191; rows around it and the last row are checked bit for bit
+    # 8200 x 65536 activations (2.15 GB of fp32, past 2^31 bytes): the
+    # quantizer indexes with 64 bits in one launch; rows on both sides of the
+    # 2 GiB mark (inside row 8191) and the last row are checked bit for bit
     M, K = 8200, 65536
-    say("q8_1 M=%d K=%d (two launches)" % (M, K))
+    say("q8_1 M=%d K=%d (past 2 GiB of input)" % (M, K))
     g = torch.Generator(device="cuda").manual_seed(31)
     x = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32)
     qa_g, ds_g = q4.q8_1_quantize(x)
@@ -198,7 +198,11 @@ def gemv_case_check(q4, orc, M, N, K, seed, what, rows=None):
     sm_h = sm.cpu().view(torch.int16).numpy().view(np.uint16)
     yh = y.cpu().numpy()
     if rows is None:
-        ref = orc.q4_gemv(x.numpy(), qs_h, sm_h, K)
+        # the oracle packs W itself: the GPU's packing must agree before its
+        # codes feed the oracle's product
+        qs_o, sm_o = orc.q4_pack(W.numpy())
+        assert_pack_equal(qs_o, sm_o, qs, sm, what)
+        ref = orc.q4_gemv(x.numpy(), qs_o, sm_o, K)
         close(yh, ref, what)
     else:
         # the oracle packs its own copy of the sampled rows from W
@@ -332,17 +336,27 @@ def test_mmq_parity_small(q4, orc, M, N, K, outl):
 
 def test_mmq_512_full(q4, orc):
     c = wl.MMQ_512
-    say("mmq M=512 K=2560 N=9216 (sampled activation rows)")
-    rows = np.unique(np.concatenate([[0, 511], np.random.default_rng(1).choice(512, 126, replace=False)]))
-    mmq_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq 512", mrows=rows)
+    say("mmq M=512 K=2560 N=9216 (every output)")
+    mmq_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq 512")
 
 
 @pytest.mark.parametrize("idx", [0, 1])
 def test_mmq_2048_full(q4, orc, idx):
+    # every output of the layer (the oracle needs a few seconds on 16 threads)
     c = wl.MMQ_2048[idx]
-    say("mmq M=2048 %s K=%d N=%d (sampled activation rows)" % (c["name"], c["K"], c["N"]))
-    rows = np.unique(np.concatenate([[0, 2047], np.random.default_rng(2 + idx).choice(2048, 62, replace=False)]))
-    mmq_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq 2048 " + c["name"], mrows=rows)
+    say("mmq M=2048 %s K=%d N=%d (every output)" % (c["name"], c["K"], c["N"]))
+    mmq_check(q4, orc, c["M"], c["N"], c["K"], c["seed"], c["outliers"], "mmq 2048 " + c["name"])
+
+
+def test_mmq_pp1024_gate_up(q4, orc):
+    # the prefill sweep's pp = 1024 point on the 4096 -> 12288 layer: 768
+    # tiles of 128 x 128, so the int8 design runs unsplit with 16 groups per
+    # tile (every other int8 test with more than two groups per tile splits K)
+    c = wl.MMQ_2048[0]
+    M = 1024
+    assert q4.q4_mmq_workspace_bytes(M, c["N"], c["K"]) == 0
+    say("mmq pp1024 gate_up M=%d K=%d N=%d (every output)" % (M, c["K"], c["N"]))
+    mmq_check(q4, orc, M, c["N"], c["K"], c["seed"], True, "mmq pp1024 gate_up")
 
 
 def test_mmq_split_k_small(q4, orc):
