@@ -21,11 +21,17 @@ the MMQ TOPS (2 M N K / kernel time) are reported under "mmq_prefill".
 Algorithmic bytes of a GEMV: packed weights N*K/2 + scales N*K/256*4 + x M*K*4
 + y M*N*4.  Packing (q4_pack) is setup and is not timed.
 
+Both MMQ designs run in the step: q4_mmq_gemm as routed (the fp16 matrix-core
+design at these shapes) and q4_mmq_gemm_int8 (int8 matrix cores, exact int32
+block dots); each is reported against its own matrix-core peak.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --pmc-mmq        (Q8_1 + MMQ, M=2048 4096->12288, 3 launches;
                                          nothing printed)
-       python bench.py --pmc-workload   (lm_head GEMV and a 256 MiB copy, 3 launches
-                                         each, for hardware-counter runs; prints nothing)
+       python bench.py --pmc-mmq-int8   (the same through q4_mmq_gemm_int8)
+       python bench.py --pmc-workload   (lm_head GEMV over two weight copies in turn,
+                                         4 launches, and a 256 MiB copy, 3 launches,
+                                         for hardware-counter runs; prints nothing)
 """
 import hashlib
 import argparse
@@ -75,6 +81,8 @@ def parse():
                     help="only launch the lm_head GEMV and a 256 MiB copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-mmq", action="store_true",
                     help="only launch Q8_1 + MMQ on the M=2048, 4096 -> 12288 layer, 3 times (for rocprofv3 --pmc)")
+    ap.add_argument("--pmc-mmq-int8", action="store_true",
+                    help="as --pmc-mmq through q4_mmq_gemm_int8 (the int8 matrix-core design)")
     return ap.parse_args()
 
 
@@ -111,20 +119,23 @@ def measured_traffic():
 
 
 def pmc_workload():
-    """lm_head GEMV x3 and a 256 MiB device copy x3, nothing timed or printed."""
+    """lm_head GEMV over two weight copies in turn (402 MB together, beyond the
+    256 MB Infinity Cache) x4 and a 256 MiB device copy x3; nothing timed or
+    printed."""
     import torch
     import bit_quantized_matmul_q4_amd as q4
     from bit_quantized_matmul_q4_amd import workloads as wl
     dev = torch.device("cuda:0")
     _, K, N = wl.DECODE_PROJECTIONS[7]
-    g = wl.generator(7, dev)
-    W = wl.draw_weights(g, N, K, dev)
-    qs, sm = q4.q4_pack(W)
-    del W
+    copies = []
+    for i in range(2):
+        W = wl.draw_weights(wl.generator(7 + 100 * i, dev), N, K, dev)
+        copies.append(q4.q4_pack(W))
+        del W
     x = wl.draw_activations(wl.generator(12345, dev), 1, K, False, dev)
     y = torch.empty((1, N), dtype=torch.float32, device=dev)
-    for _ in range(3):
-        q4.q4_gemv(x, qs, sm, y=y)
+    for i in range(4):
+        q4.q4_gemv(x, *copies[i % 2], y=y)
     src = torch.ones((64 << 20,), dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -132,8 +143,9 @@ def pmc_workload():
     torch.cuda.synchronize()
 
 
-def pmc_mmq():
-    """Q8_1 + MMQ on the M = 2048, 4096 -> 12288 prefill layer x3, nothing timed or printed."""
+def pmc_mmq(int8=False):
+    """Q8_1 + MMQ on the M = 2048, 4096 -> 12288 prefill layer x3 (q4_mmq_gemm,
+    or q4_mmq_gemm_int8), nothing timed or printed."""
     import torch
     import bit_quantized_matmul_q4_amd as q4
     from bit_quantized_matmul_q4_amd import workloads as wl
@@ -143,10 +155,21 @@ def pmc_mmq():
     qs, sm = q4.q4_pack(W)
     del W
     y = torch.empty((c["M"], c["N"]), dtype=torch.float32, device=dev)
+    gemm = q4.q4_mmq_gemm_int8 if int8 else q4.q4_mmq_gemm
     for _ in range(3):
         qa, ds = q4.q8_1_quantize(x)
-        q4.q4_mmq_gemm(qa, ds, qs, sm, y=y)
+        gemm(qa, ds, qs, sm, y=y)
     torch.cuda.synchronize()
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl):
@@ -154,7 +177,8 @@ def cpu_baseline(wl):
     import numpy as np
     from oracle import oracle as orc
     threads = orc.get_threads()
-    out = {"kind": "oracle", "cores": threads}
+    out = {"kind": "oracle", "cores": threads, "cpu_model": cpu_model(),
+           "affinity_cpus": len(os.sched_getaffinity(0))}
     # GEMV: the oracle's fp64 GEMV on a sample of the decode projection set (one
     # layer's q, k, v, o, gate, up, down at M = 1), packing excluded from timing
     cases = []
@@ -426,8 +450,8 @@ def main():
               "(the multi-GPU sharding is a design note, not an implementation)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
-    if args.pmc_mmq:
-        pmc_mmq()
+    if args.pmc_mmq or args.pmc_mmq_int8:
+        pmc_mmq(int8=args.pmc_mmq_int8)
         return
     if args.pmc_workload:
         pmc_workload()
@@ -492,7 +516,10 @@ def main():
         y = torch.empty((c["M"], c["N"]), dtype=torch.float32, device=dev)
         ws_n = q4.q4_mmq_workspace_bytes(c["M"], c["N"], c["K"])
         ws = torch.empty((max(ws_n, 1),), dtype=torch.uint8, device=dev)
-        pre.append((c, x, qa, ds, qs, sm, y, ws))
+        wi_n = q4.q4_mmq_int8_workspace_bytes(c["M"], c["N"], c["K"])
+        wi = torch.empty((max(wi_n, 1),), dtype=torch.uint8, device=dev)
+        yi = torch.empty((c["M"], c["N"]), dtype=torch.float32, device=dev)
+        pre.append((c, x, qa, ds, qs, sm, y, ws, yi, wi))
     # a plain device copy of known size: reference for the HBM byte counters
     cp_src = torch.empty((64 << 20,), dtype=torch.float32, device=dev).fill_(1.0)
     cp_dst = torch.empty_like(cp_src)
@@ -532,13 +559,15 @@ def main():
         lm_head()
         ev[2].record(stream)
         i = 3
-        for (c, x, qa, ds, qs, sm, y, ws) in pre:
+        for (c, x, qa, ds, qs, sm, y, ws, yi, wi) in pre:
             ev[i].record(stream)
             q4.q8_1_quantize(x, qa, ds)
             ev[i + 1].record(stream)
             q4.q4_mmq_gemm(qa, ds, qs, sm, y=y, workspace=ws)
             ev[i + 2].record(stream)
-            i += 4  # (the 4th slot keeps the layout uniform)
+            q4.q4_mmq_gemm_int8(qa, ds, qs, sm, y=yi, workspace=wi)
+            ev[i + 3].record(stream)
+            i += 4
         return ev
 
     for _ in range(args.warmup):
@@ -567,6 +596,7 @@ def main():
         i = 3 + 4 * k
         q_ms = med([e[i].elapsed_time(e[i + 1]) for e in events])
         g_ms = med([e[i + 1].elapsed_time(e[i + 2]) for e in events])
+        i_ms = med([e[i + 2].elapsed_time(e[i + 3]) for e in events])
         ops = 2.0 * c["M"] * c["N"] * c["K"]
         mmq_rep["M%d_%s" % (c["M"], c["name"])] = {
             "M": c["M"], "K": c["K"], "N": c["N"],
@@ -578,6 +608,8 @@ def main():
             "q8_1_us": round(q_ms * 1e3, 2),
             "q8_1_gbs": round(q8_bytes(c["M"], c["K"]) / (q_ms * 1e-3) / 1e9, 1),
             "tops_incl_q8_1": round(ops / ((g_ms + q_ms) * 1e-3) / 1e12, 2),
+            "int8_design": {"mmq_us": round(i_ms * 1e3, 2), "tops": round(ops / (i_ms * 1e-3) / 1e12, 2),
+                            "frac_i8_peak": round(ops / (i_ms * 1e-3) / 1e12 / I8_PEAK_TOPS, 4)},
         }
     step_ms = wall / args.steps * 1e3
     value = decode_bytes / (decode_ms * 1e-3) / 1e9
@@ -595,8 +627,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4 x f16 -> f32 (GEMV); f16 x f16 -> f32 (MMQ on fp16 matrix cores, Q8_1 and u4 operands "
-                 "scaled into fp16)",
+        "dtype": "u4 x f16 -> f32 (GEMV); MMQ: f16 x f16 -> f32 (q4_mmq_gemm at these shapes: Q8_1 and u4 "
+                 "operands scaled into fp16) and i8 x i4 -> i32 -> f32 (q4_mmq_gemm_int8: exact block dots)",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; random weights of the stated shapes)",
         "config": {
             "workload": "decode token of a ~4B dense transformer at M=1: 36 layers x "
@@ -613,6 +645,7 @@ def main():
             "lm_head_us": round(lm_ms * 1e3, 2),
             "lm_head_gbs": round(lm_gbs, 1),
             "tokens_per_s_weights_only": round(1e3 / decode_ms, 1),
+            "frac_hbm": round(value / HBM_PEAK_GBS, 4),
         },
         "roofline": {
             "kernel": "k_gemv_dot2 (lm_head launch, M=1, K=2560, N=151936)",
@@ -627,7 +660,11 @@ def main():
             "kernel": "q4_mmq_gemm, fp16 design: k_mmqf_rowscale + k_mmqf_image + k_mmqf "
                       "(M=2048, K=4096, N=12288)", "bound": "mfma",
             "achieved": big["tops"], "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(big["tops"] / F16_PEAK_TFLOPS, 4)}),
+            "frac": round(big["tops"] / F16_PEAK_TFLOPS, 4)},
+            roofline_int8={
+                "kernel": "q4_mmq_gemm_int8: k_mmq (M=2048, K=4096, N=12288)", "bound": "mfma",
+                "achieved": big["int8_design"]["tops"], "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": big["int8_design"]["frac_i8_peak"]}),
     }
     n_unfused = LAYERS * len(layers[0])
     unf_us = graph_launch_us(decode_layers_unfused, n_unfused, stream) * n_unfused

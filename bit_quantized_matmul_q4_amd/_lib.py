@@ -28,6 +28,7 @@ SYMBOLS = [
     "q4_abi_version", "q4_strerror", "q4_pack", "q8_1_quantize", "q4_gemv_workspace_bytes",
     "q4_gemv", "q4_mmq_workspace_bytes", "q4_mmq_gemm", "q4_mmq_gemm_q8_1", "q4_mmq_block_dots",
     "q4_pack_g32", "q4_gemv_g32_workspace_bytes", "q4_gemv_g32", "q4_mmq_gemm_g32",
+    "q4_mmq_int8_workspace_bytes", "q4_mmq_gemm_int8",
 ]
 
 _lib = None
@@ -64,6 +65,8 @@ def lib():
         "q4_gemv_g32_workspace_bytes": ([I64, I64, I64], SZ),
         "q4_gemv_g32": ([P, I64, P, P, I64, I64, P, P, SZ, P], I),
         "q4_mmq_gemm_g32": ([P, P, I64, P, P, I64, I64, P, P, SZ, P], I),
+        "q4_mmq_int8_workspace_bytes": ([I64, I64, I64], SZ),
+        "q4_mmq_gemm_int8": ([P, P, I64, P, P, I64, I64, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -217,6 +220,27 @@ def q4_mmq_gemm(qa, ds, qs, sm, y=None, workspace=None, stream=None):
     ws, wsb = _workspace(q4_mmq_workspace_bytes(M, N, K), workspace, qa.device)
     _check(lib().q4_mmq_gemm(_ptr(qa), _ptr(ds), M, _ptr(qs), _ptr(sm), N, K, _ptr(y), _ptr(ws),
                              wsb, _stream(stream, qa)), "q4_mmq_gemm")
+    return y
+
+
+def q4_mmq_int8_workspace_bytes(M, N, K):
+    return lib().q4_mmq_int8_workspace_bytes(int(M), int(N), int(K))
+
+
+def q4_mmq_gemm_int8(qa, ds, qs, sm, y=None, workspace=None, stream=None):
+    """q4_mmq_gemm on the int8 matrix-core design at any shape."""
+    M, K = qa.shape
+    N = qs.shape[0]
+    _need(qa, torch.int8, (M, K), "qa")
+    _need(ds, torch.float16, (M, K // 32, 2), "ds")
+    _need(qs, torch.uint8, (N, K // 2), "qs")
+    _need(sm, torch.float16, (N, K // 256, 2), "sm")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=qa.device)
+    _need(y, torch.float32, (M, N), "y")
+    ws, wsb = _workspace(q4_mmq_int8_workspace_bytes(M, N, K), workspace, qa.device)
+    _check(lib().q4_mmq_gemm_int8(_ptr(qa), _ptr(ds), M, _ptr(qs), _ptr(sm), N, K, _ptr(y), _ptr(ws),
+                                  wsb, _stream(stream, qa)), "q4_mmq_gemm_int8")
     return y
 
 

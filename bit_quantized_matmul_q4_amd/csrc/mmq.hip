@@ -616,18 +616,22 @@ bool mmq_uses_f16(int64_t M, int64_t N, int64_t K)
     return tiles * 5 >= slots * 4;
 }
 
+size_t mmq_int8_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 1 || N < 1 || K < kGroup) return 0;
+    const SplitCfg sc = choose_split(M, N, (int)K);
+    if (sc.nsplit == 1) return 0;
+    // the largest sub-problem's partials (sub-problems split at < 2 GiB reach)
+    const int64_t n_max = ((kMaxBufferBytes - 1) / (K / 2)) / kTile * kTile;
+    const int64_t m_max = ((kMaxBufferBytes - 1) / K) / kTile * kTile;
+    const int64_t mm = M < m_max ? M : m_max, nn = N < n_max ? N : n_max;
+    return (size_t)sc.nsplit * mm * nn * sizeof(float);
+}
+
 size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < kGroup) return 0;
-    size_t need = 0;
-    const SplitCfg sc = choose_split(M, N, (int)K);
-    if (sc.nsplit > 1) {
-        // the largest sub-problem's partials (sub-problems split at < 2 GiB reach)
-        const int64_t n_max = ((kMaxBufferBytes - 1) / (K / 2)) / kTile * kTile;
-        const int64_t m_max = ((kMaxBufferBytes - 1) / K) / kTile * kTile;
-        const int64_t mm = M < m_max ? M : m_max, nn = N < n_max ? N : n_max;
-        need = (size_t)sc.nsplit * mm * nn * sizeof(float);
-    }
+    size_t need = mmq_int8_workspace_bytes(M, N, K);
     if (mmq_uses_f16(M, N, K)) {
         const size_t f = mmqf_workspace_bytes(M, K);
         if (f > need) need = f;
@@ -641,6 +645,14 @@ hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uin
 {
     if (mmq_uses_f16(M, N, K))
         return launch_mmqf(qa, ds, M, qs, sm, N, K, false, y, nullptr, nullptr, workspace, stream);
+    return run_tiles(kOutY, false, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
+                     dev.num_cus, stream);
+}
+
+hipError_t launch_mmq_int8(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                           const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
+                           const DeviceInfo &dev, hipStream_t stream)
+{
     return run_tiles(kOutY, false, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
                      dev.num_cus, stream);
 }

@@ -153,14 +153,10 @@ int q4_gemv_g32(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm
     return gemv_common(x, M, qs, sm, N, K, 32, y, workspace, ws_bytes, stream);
 }
 
-size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)
-{
-    if (M < 0 || M > Q4_MAX_M_MMQ || N < 0 || N > Q4_MAX_N || !valid_k(K, 256)) return 0;
-    return q4mi::mmq_workspace_bytes(M, N, K);
-}
+enum MmqRoute { kRouteShape, kRouteShapeG32, kRouteInt8 };
 
 static int mmq_common(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
-                      const uint16_t *sm, int64_t N, int64_t K, bool g32, float *y, void *workspace,
+                      const uint16_t *sm, int64_t N, int64_t K, MmqRoute route, float *y, void *workspace,
                       size_t ws_bytes, void *stream)
 {
     if (M < 0 || M > Q4_MAX_M_MMQ || N < 0 || N > Q4_MAX_N || !valid_k(K, 256)) return Q4_ERR_ARG;
@@ -168,29 +164,45 @@ static int mmq_common(const int8_t *qa, const uint16_t *ds, int64_t M, const uin
     if (!qa || !ds || !qs || !sm || !y) return Q4_ERR_ARG;
     if (!aligned(qa, 16) || !aligned(ds, 4) || !aligned(qs, 16) || !aligned(sm, 4) || !aligned(y, 4))
         return Q4_ERR_ALIGN;
-    const size_t need = q4mi::mmq_workspace_bytes(M, N, K);
+    const size_t need =
+        route == kRouteInt8 ? q4mi::mmq_int8_workspace_bytes(M, N, K) : q4mi::mmq_workspace_bytes(M, N, K);
     if (need > 0 && (!workspace || ws_bytes < need)) return Q4_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 16)) return Q4_ERR_ALIGN;
     const DeviceInfo *dev = nullptr;
     if (int rc = current_device(&dev)) return rc;
-    return launch_status(g32 ? q4mi::launch_mmq_g32(qa, ds, M, qs, sm, N, (int)K, y, workspace, *dev,
-                                                    (hipStream_t)stream)
-                             : q4mi::launch_mmq(qa, ds, M, qs, sm, N, (int)K, y, workspace, *dev,
-                                                (hipStream_t)stream));
+    hipStream_t st = (hipStream_t)stream;
+    switch (route) {
+    case kRouteShapeG32: return launch_status(q4mi::launch_mmq_g32(qa, ds, M, qs, sm, N, (int)K, y, workspace, *dev, st));
+    case kRouteInt8: return launch_status(q4mi::launch_mmq_int8(qa, ds, M, qs, sm, N, (int)K, y, workspace, *dev, st));
+    default: return launch_status(q4mi::launch_mmq(qa, ds, M, qs, sm, N, (int)K, y, workspace, *dev, st));
+    }
 }
 
 int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                 const uint16_t *sm, int64_t N, int64_t K, float *y, void *workspace,
                 size_t ws_bytes, void *stream)
 {
-    return mmq_common(qa, ds, M, qs, sm, N, K, false, y, workspace, ws_bytes, stream);
+    return mmq_common(qa, ds, M, qs, sm, N, K, kRouteShape, y, workspace, ws_bytes, stream);
 }
 
 int q4_mmq_gemm_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                     const uint16_t *sm, int64_t N, int64_t K, float *y, void *workspace,
                     size_t ws_bytes, void *stream)
 {
-    return mmq_common(qa, ds, M, qs, sm, N, K, true, y, workspace, ws_bytes, stream);
+    return mmq_common(qa, ds, M, qs, sm, N, K, kRouteShapeG32, y, workspace, ws_bytes, stream);
+}
+
+size_t q4_mmq_int8_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || M > Q4_MAX_M_MMQ || N < 0 || N > Q4_MAX_N || !valid_k(K, 256)) return 0;
+    return q4mi::mmq_int8_workspace_bytes(M, N, K);
+}
+
+int q4_mmq_gemm_int8(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                     const uint16_t *sm, int64_t N, int64_t K, float *y, void *workspace,
+                     size_t ws_bytes, void *stream)
+{
+    return mmq_common(qa, ds, M, qs, sm, N, K, kRouteInt8, y, workspace, ws_bytes, stream);
 }
 
 int q4_mmq_gemm_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,

@@ -33,6 +33,11 @@ hipError_t launch_gemv(const float *x, int M, const uint8_t *qs, const uint16_t 
                        hipStream_t stream);
 
 size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// the int8 matrix-core design on its own, at any shape (K-split partials only)
+size_t mmq_int8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_mmq_int8(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                           const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
+                           const DeviceInfo &dev, hipStream_t stream);
 hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                       const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
                       const DeviceInfo &dev, hipStream_t stream);

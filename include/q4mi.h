@@ -233,6 +233,33 @@ int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *
                 size_t ws_bytes, void *stream);
 
 /*
+ * q4_mmq_gemm_int8 -- q4_mmq_gemm on int8 matrix cores at every shape: the
+ * hipfire note's MMQ arithmetic as written ("list of changes": Q8_1
+ * pre-quantized activations, LDS-staged tiles, i8 matrix products over
+ * 128x128 output tiles).  Each 32-wide block product
+ *     I[m][n][b] = sum_{k in block b} a[m][k] * (q[n][k] - 8)
+ * is an exact int32 from one int8 MFMA; the eight blocks of a weight group
+ * are combined in int32 with each row's block scales as 13-bit integers
+ * relative to the group's largest (D = rint(d / step), step = max d / 8191),
+ * and the group's scale, step and minimum term are applied in fp32:
+ *     y[m][n] = sum_g ( scale * step * sum_b D * I + (minimum + 8 scale) * X[m][g] ),
+ *     X[m][g] = sum_{b in g} d[m][b] * sum_{k in b} a[m][k].
+ * Every activation may move by up to 1/16382 of the largest |x| in its group
+ * of 256 on top of Q8_1's own rounding; results match the fp64 definition to
+ * max|dy| / max|y| <= 2e-3 and NMSE <= 1e-6 (measured NMSE ~3e-8 on N(0,1)
+ * activations with outliers up to 1000x).  Reruns are bit-identical.  Grids
+ * with at most one 128 x 128 tile per CU split K over workgroups into fp32
+ * partials in the workspace, summed in split order by a second kernel.
+ *   Arguments, layouts and errors as q4_mmq_gemm; workspace: at least
+ *   q4_mmq_int8_workspace_bytes(M, N, K) bytes (0 when K is not split; pure
+ *   host function, 0 for shapes the call would reject).
+ */
+size_t q4_mmq_int8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int q4_mmq_gemm_int8(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                     const uint16_t *sm, int64_t N, int64_t K, float *y, void *workspace,
+                     size_t ws_bytes, void *stream);
+
+/*
  * q4_mmq_gemm_q8_1 -- q4_mmq_gemm whose epilogue hands its result on as Q8_1
  * activations for a following MMQ layer instead of writing fp32: the
  * quantization step that the hipfire MMQ note runs ahead of the prefill GEMM

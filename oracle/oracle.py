@@ -80,12 +80,12 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
-    # thread count: the cores this process may run on, at most 16
+    # thread count: every core this process may run on
     try:
         ncpu = len(os.sched_getaffinity(0))
     except AttributeError:
         ncpu = os.cpu_count() or 1
-    lib.orc_set_threads(max(1, min(16, ncpu)))
+    lib.orc_set_threads(max(1, ncpu))
     _lib = lib
     return lib
 

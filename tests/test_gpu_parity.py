@@ -359,6 +359,40 @@ def test_mmq_pp1024_gate_up(q4, orc):
     mmq_check(q4, orc, M, c["N"], c["K"], c["seed"], True, "mmq pp1024 gate_up")
 
 
+INT8_FULL = [dict(wl.MMQ_512, name="m512")] + wl.MMQ_2048
+
+
+@pytest.mark.parametrize("idx", range(len(INT8_FULL)))
+def test_mmq_int8_design_full(q4, orc, idx):
+    # q4_mmq_gemm_int8 at the prefill configs, where q4_mmq_gemm takes the
+    # fp16 design: exact int32 block dots on int8 matrix cores, every output
+    c = INT8_FULL[idx]
+    say("mmq int8 design M=%d K=%d N=%d (every output)" % (c["M"], c["K"], c["N"]))
+    W, x = wl.mmq_case(c["seed"], c["M"], c["N"], c["K"], c["outliers"])
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    y = q4.q4_mmq_gemm_int8(qa, ds, qs, sm)
+    torch.cuda.synchronize()
+    qs_o, sm_o = orc.q4_pack(W.numpy())
+    assert_pack_equal(qs_o, sm_o, qs, sm, "int8 design pack")
+    qa_o, ds_o = orc.q8_1_quantize(x.numpy())
+    assert np.array_equal(qa.cpu().numpy(), qa_o)
+    assert np.array_equal(ds.cpu().view(torch.int16).numpy().view(np.uint16), ds_o)
+    close(y.cpu().numpy(), orc.q4_mmq(qa_o, ds_o, qs_o, sm_o, c["K"]), "mmq int8 design " + c["name"])
+
+
+@pytest.mark.parametrize("M,N,K", [(100, 224, 2048), (1024, 12288, 4096), (257, 385, 1024)])
+def test_mmq_int8_entry_matches_routed_int8(q4, orc, M, N, K):
+    # where q4_mmq_gemm routes to the int8 design (K split, unsplit, ragged),
+    # q4_mmq_gemm_int8 runs the same kernels: identical bits
+    say("mmq int8 entry vs routed int8 M=%d N=%d K=%d" % (M, N, K))
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == q4.q4_mmq_int8_workspace_bytes(M, N, K)
+    W, x = wl.mmq_case(M + N + K, M, N, K, True)
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    assert torch.equal(q4.q4_mmq_gemm_int8(qa, ds, qs, sm), q4.q4_mmq_gemm(qa, ds, qs, sm))
+
+
 def test_mmq_split_k_small(q4, orc):
     # 2 output tiles and 8 groups of K: the launch splits K four ways and sums
     # the partials in a second pass
