@@ -6,12 +6,14 @@ include/q4mi.h); this package is the Python binding of that ABI.
 """
 from ._lib import (  # noqa: F401
     GEMV_MAX_M,
+    NOALLOC_SCRATCH_BYTES,
     Q4Error,
     lib,
     q4_abi_version,
     q4_gemv,
     q4_gemv_g32,
     q4_gemv_g32_workspace_bytes,
+    q4_gemv_noalloc,
     q4_gemv_workspace_bytes,
     q4_mmq_block_dots,
     q4_mmq_gemm,

@@ -28,8 +28,9 @@ SYMBOLS = [
     "q4_abi_version", "q4_strerror", "q4_pack", "q8_1_quantize", "q4_gemv_workspace_bytes",
     "q4_gemv", "q4_mmq_workspace_bytes", "q4_mmq_gemm", "q4_mmq_gemm_q8_1", "q4_mmq_block_dots",
     "q4_pack_g32", "q4_gemv_g32_workspace_bytes", "q4_gemv_g32", "q4_mmq_gemm_g32",
-    "q4_mmq_int8_workspace_bytes", "q4_mmq_gemm_int8",
+    "q4_gemv_noalloc", "q4_mmq_int8_workspace_bytes", "q4_mmq_gemm_int8",
 ]
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -65,6 +66,7 @@ def lib():
         "q4_gemv_g32_workspace_bytes": ([I64, I64, I64], SZ),
         "q4_gemv_g32": ([P, I64, P, P, I64, I64, P, P, SZ, P], I),
         "q4_mmq_gemm_g32": ([P, P, I64, P, P, I64, I64, P, P, SZ, P], I),
+        "q4_gemv_noalloc": ([P, I64, P, P, I64, I64, P, P], I),
         "q4_mmq_int8_workspace_bytes": ([I64, I64, I64], SZ),
         "q4_mmq_gemm_int8": ([P, P, I64, P, P, I64, I64, P, P, SZ, P], I),
     }
@@ -169,6 +171,20 @@ def q4_gemv(x, qs, sm, y=None, workspace=None, stream=None):
     ws, wsb = _workspace(q4_gemv_workspace_bytes(M, N, K), workspace, x.device)
     _check(lib().q4_gemv(_ptr(x), M, _ptr(qs), _ptr(sm), N, K, _ptr(y), _ptr(ws), wsb,
                          _stream(stream, x)), "q4_gemv")
+    return y
+
+
+def q4_gemv_noalloc(x, qs, sm, y, stream=None):
+    """q4_gemv with the K-split partials in the library's fixed device array
+    (no workspace); y fp32 [M][N] must be given."""
+    M, K = x.shape
+    N = qs.shape[0]
+    _need(x, torch.float32, (M, K), "x")
+    _need(qs, torch.uint8, (N, K // 2), "qs")
+    _need(sm, torch.float16, (N, K // 256, 2), "sm")
+    _need(y, torch.float32, (M, N), "y")
+    _check(lib().q4_gemv_noalloc(_ptr(x), M, _ptr(qs), _ptr(sm), N, K, _ptr(y), _stream(stream, x)),
+           "q4_gemv_noalloc")
     return y
 
 

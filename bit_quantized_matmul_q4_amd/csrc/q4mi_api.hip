@@ -56,6 +56,38 @@ inline bool valid_k(int64_t K, int64_t unit) { return K > 0 && K <= Q4_MAX_K && 
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_LAUNCH; }
 
+// Device memory of q4_gemv_noalloc: its K-split partials live here instead of
+// in a caller's workspace.  Each device the library runs on holds its own copy
+// of the array until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: kernels and copies only ever
+// see the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[Q4_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchSlot {
+    std::once_flag once;
+    int status;  // Q4_OK or Q4_ERR_DEVICE
+    void *ptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.
+int scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q4_ERR_DEVICE;
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot]() {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        slot.ptr = p;
+        slot.status = (e == hipSuccess && p != nullptr) ? Q4_OK : Q4_ERR_DEVICE;
+    });
+    if (slot.status != Q4_OK) return slot.status;
+    *out = slot.ptr;
+    return Q4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,6 +183,33 @@ int q4_gemv_g32(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm
                 float *y, void *workspace, size_t ws_bytes, void *stream)
 {
     return gemv_common(x, M, qs, sm, N, K, 32, y, workspace, ws_bytes, stream);
+}
+
+int q4_gemv_noalloc(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N, int64_t K,
+                    float *y, void *stream)
+{
+    if (!gemv_shape_ok(M, N, K, 256)) return Q4_ERR_ARG;
+    if (M == 0 || N == 0) return Q4_OK;
+    if (!x || !qs || !sm || !y) return Q4_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(qs, 16) || !aligned(sm, 4) || !aligned(y, 4)) return Q4_ERR_ALIGN;
+    const size_t need = q4mi::gemv_workspace_bytes(M, N, K, 256);
+    if (need > (size_t)Q4_NOALLOC_SCRATCH_BYTES) return Q4_ERR_WORKSPACE;
+    const DeviceInfo *dev = nullptr;
+    if (int rc = current_device(&dev)) return rc;
+    void *ws = nullptr;
+    if (need > 0) {
+        if (int rc = scratch_address(&ws)) return rc;
+    }
+    // the partials are written in full before they are read: nothing in the
+    // array has to start at zero
+    return launch_status(q4mi::launch_gemv(x, (int)M, qs, sm, N, (int)K, 256, y, ws, need > 0 ? need : 0, *dev,
+                                           (hipStream_t)stream));
+}
+
+size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || M > Q4_MAX_M_MMQ || N < 0 || N > Q4_MAX_N || !valid_k(K, 256)) return 0;
+    return q4mi::mmq_workspace_bytes(M, N, K);
 }
 
 enum MmqRoute { kRouteShape, kRouteShapeG32, kRouteInt8 };

@@ -154,6 +154,26 @@ int q4_gemv(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, in
             int64_t K, float *y, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * q4_gemv_noalloc -- q4_gemv for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels, plan and results (bit for bit) as q4_gemv,
+ * with no workspace argument.  Shapes that split K keep their partial sums in
+ * a fixed device array of Q4_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per device, allocated when the library's code is loaded on that device and
+ * held until the process ends; the call itself allocates nothing.
+ * A shape whose q4_gemv_workspace_bytes exceeds Q4_NOALLOC_SCRATCH_BYTES is
+ * refused with Q4_ERR_WORKSPACE (use q4_gemv with a workspace).  Every call
+ * on one device shares that array: two calls that may run at the same time on
+ * one device (different streams, or graphs replayed concurrently) race and
+ * must be ordered by the caller.  Nothing in the array needs to start at
+ * zero (each call writes every partial it later reads).
+ * Arguments and errors otherwise as q4_gemv.
+ */
+#define Q4_NOALLOC_SCRATCH_BYTES (32u << 20)
+int q4_gemv_noalloc(const float *x, int64_t M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                    int64_t K, float *y, void *stream);
+
+/*
  * Group-32 variant (the "W4A16, asymmetric, group 32" int4 checkpoints the vLLM
  * ROCM_OCTAVE pull request validates on, "Validation" and the QSA evaluation
  * setup).  The code bytes qs are laid out exactly as for group 256; the

@@ -158,3 +158,13 @@ def test_gemv_output_beyond_one_descriptor_rejected():
     assert q4.q4_gemv_workspace_bytes(16, 40000000, 256) == 0
     # one activation row on the VALU arm writes y with 64-bit indexing: allowed
     assert q4.q4_gemv_workspace_bytes(1, 40000000, 256) == 0
+
+
+def test_gemv_noalloc_validates_before_any_device_call():
+    L = q4.lib()
+    # more K-split partials than the library's fixed scratch array holds
+    assert q4.q4_gemv_workspace_bytes(16, 151936, 65536) > q4.NOALLOC_SCRATCH_BYTES
+    assert L.q4_gemv_noalloc(FAKE, 16, FAKE, FAKE, 151936, 65536, FAKE, NULL) == WORKSPACE
+    assert L.q4_gemv_noalloc(FAKE, 17, FAKE, FAKE, 8, 256, FAKE, NULL) == ARG
+    assert L.q4_gemv_noalloc(ODD, 1, FAKE, FAKE, 8, 256, FAKE, NULL) == ALIGN
+    assert L.q4_gemv_noalloc(NULL, 0, NULL, NULL, 8, 256, NULL, NULL) == 0
