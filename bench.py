@@ -662,7 +662,7 @@ def main():
             "achieved": big["tops"], "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(big["tops"] / F16_PEAK_TFLOPS, 4)},
             roofline_int8={
-                "kernel": "q4_mmq_gemm_int8: k_mmq (M=2048, K=4096, N=12288)", "bound": "mfma",
+                "kernel": "q4_mmq_gemm_int8: k_mmqi_prep + k_mmqi (M=2048, K=4096, N=12288)", "bound": "mfma",
                 "achieved": big["int8_design"]["tops"], "peak": I8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": big["int8_design"]["frac_i8_peak"]}),
     }

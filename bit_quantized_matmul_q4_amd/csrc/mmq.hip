@@ -616,9 +616,20 @@ bool mmq_uses_f16(int64_t M, int64_t N, int64_t K)
     return tiles * 5 >= slots * 4;
 }
 
+// The int8 design's fp32-output kernels: the pipelined k_mmqi (mmq_i8.hip,
+// 128 x 256 tiles, one workgroup per CU) when its grid covers at least half
+// the CUs, otherwise k_mmq here (128 x 128 tiles, two per CU, K split for
+// small grids).  A function of the shape only.
+bool mmq_int8_pipelined(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t tiles = ((M + 255) / 256) * ((N + 127) / 128);
+    return tiles >= 128 && mmqi_supported(M, N, K);
+}
+
 size_t mmq_int8_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < kGroup) return 0;
+    if (mmq_int8_pipelined(M, N, K)) return mmqi_workspace_bytes(M, N, K);
     const SplitCfg sc = choose_split(M, N, (int)K);
     if (sc.nsplit == 1) return 0;
     // the largest sub-problem's partials (sub-problems split at < 2 GiB reach)
@@ -631,12 +642,33 @@ size_t mmq_int8_workspace_bytes(int64_t M, int64_t N, int64_t K)
 size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < kGroup) return 0;
+    // the K-split partials of k_mmq (Q8_1 output and group-32 weights take it
+    // at any grid), the records of k_mmqi, the fp16 design's image
     size_t need = mmq_int8_workspace_bytes(M, N, K);
+    {
+        const SplitCfg sc = choose_split(M, N, (int)K);
+        if (sc.nsplit > 1) {
+            const int64_t n_max = ((kMaxBufferBytes - 1) / (K / 2)) / kTile * kTile;
+            const int64_t m_max = ((kMaxBufferBytes - 1) / K) / kTile * kTile;
+            const int64_t mm = M < m_max ? M : m_max, nn = N < n_max ? N : n_max;
+            const size_t part = (size_t)sc.nsplit * mm * nn * sizeof(float);
+            if (part > need) need = part;
+        }
+    }
     if (mmq_uses_f16(M, N, K)) {
         const size_t f = mmqf_workspace_bytes(M, K);
         if (f > need) need = f;
     }
     return need;
+}
+
+hipError_t launch_mmq_int8(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                           const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
+                           const DeviceInfo &dev, hipStream_t stream)
+{
+    if (mmq_int8_pipelined(M, N, K)) return launch_mmqi(qa, ds, M, qs, sm, N, K, y, workspace, stream);
+    return run_tiles(kOutY, false, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
+                     dev.num_cus, stream);
 }
 
 hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
@@ -645,16 +677,7 @@ hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uin
 {
     if (mmq_uses_f16(M, N, K))
         return launch_mmqf(qa, ds, M, qs, sm, N, K, false, y, nullptr, nullptr, workspace, stream);
-    return run_tiles(kOutY, false, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
-                     dev.num_cus, stream);
-}
-
-hipError_t launch_mmq_int8(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
-                           const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
-                           const DeviceInfo &dev, hipStream_t stream)
-{
-    return run_tiles(kOutY, false, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
-                     dev.num_cus, stream);
+    return launch_mmq_int8(qa, ds, M, qs, sm, N, K, y, workspace, dev, stream);
 }
 
 hipError_t launch_mmq_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,

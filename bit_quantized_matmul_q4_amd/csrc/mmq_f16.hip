@@ -179,44 +179,6 @@ __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restri
     }
 }
 
-// LDS byte address of a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// Loads straight into LDS: lane i's 16 (4) bytes at buffer offset voff + soff go to
-// LDS byte address base + 16 i (4 i); soff and base are the same for the
-// whole wave.
-// Written as asm so that the compiler neither tracks nor waits for them: the
-// kernel orders them itself with wait_vm_barrier.  No registers are written.
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t base)
-{
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-                 :
-                 : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(base)),
-                   "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t base)
-{
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, %3 offen lds"
-                 :
-                 : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(base)),
-                   "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "memory", "m0");
-}
-
-// Wait until at most kN vector-memory loads of this wave are outstanding,
-// then a workgroup barrier; no memory access moves across it.
-template <int kN>
-__device__ __forceinline__ void wait_vm_barrier()
-{
-    static_assert(kN >= 0 && kN < 64, "vmcnt is 6 bits");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(kN) : "memory");
-}
-
 // y (row stride ldy) for activation rows [0, M) and weight rows [0, N) of
 // this sub-problem; img/fs are its activation image and row factors.
 // Output modes: fp32 y, or y quantized to Q8_1 along n (qo int8 [M][ldy],

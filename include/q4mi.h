@@ -203,9 +203,9 @@ int q4_mmq_gemm_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8
  * q4_mmq_workspace_bytes -- device workspace q4_mmq_gemm (and
  * q4_mmq_gemm_q8_1, q4_mmq_gemm_g32) needs for this shape: the fp16
  * activation image of the fp16 path (2 * K bytes per activation row, at
- * most 256 MiB + 2 * K * 256 bytes, plus 4 bytes per row), or the K-split
- * partial sums of the int8 path (0 when K is not split).  Pure host
- * function.  Returns 0 for shapes q4_mmq_gemm would reject.
+ * most 256 MiB + 2 * K * 256 bytes, plus 4 bytes per row), or what the int8
+ * path needs (q4_mmq_int8_workspace_bytes).  Pure host function.  Returns 0
+ * for shapes q4_mmq_gemm would reject.
  */
 size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -229,9 +229,9 @@ size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *     2^-28 of their row's largest are fp16 subnormals, exact to 2^-25
  *     absolute.  Measured
  *     NMSE ~8e-8, max|dy| / max|y| ~3e-4.
- *   - int8 matrix cores elsewhere (small grids, which it splits along K):
+ *   - int8 matrix cores elsewhere, as q4_mmq_gemm_int8:
  *     per-block products sum_{k in block} a * (q - 8) are exact int32 (i8
- *     MFMA, centred codes); the eight blocks of a weight group are combined
+ *     MFMA); the eight blocks of a weight group are combined
  *     in int32 with each row's block scales as 13-bit integers relative to
  *     the group's largest (D = rint(d / step), step = max d / 8191), then
  *     the group's scale, step and minimum term are applied in fp32.  So every
@@ -267,12 +267,18 @@ int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *
  * Every activation may move by up to 1/16382 of the largest |x| in its group
  * of 256 on top of Q8_1's own rounding; results match the fp64 definition to
  * max|dy| / max|y| <= 2e-3 and NMSE <= 1e-6 (measured NMSE ~3e-8 on N(0,1)
- * activations with outliers up to 1000x).  Reruns are bit-identical.  Grids
- * with at most one 128 x 128 tile per CU split K over workgroups into fp32
- * partials in the workspace, summed in split order by a second kernel.
+ * activations with outliers up to 1000x).  Reruns are bit-identical.
+ * Grids of at least 256 tiles of 128 x 128 run a pipelined kernel whose prep
+ * pass writes, per (activation row, group), the block scales D, step, X and
+ * the centring term 8 * sum_b D * sum_{k in b} a, and per (weight row, group)
+ * scale and minimum + 8 scale in fp32, into the workspace (32 bytes per
+ * activation row and 8 bytes per weight row, per group, rows rounded up to
+ * 128).  Smaller grids split K over workgroups into fp32 partials in the
+ * workspace, summed in split order by a second kernel (no workspace when K
+ * is not split).
  *   Arguments, layouts and errors as q4_mmq_gemm; workspace: at least
- *   q4_mmq_int8_workspace_bytes(M, N, K) bytes (0 when K is not split; pure
- *   host function, 0 for shapes the call would reject).
+ *   q4_mmq_int8_workspace_bytes(M, N, K) bytes (pure host function, 0 for
+ *   shapes the call would reject).
  */
 size_t q4_mmq_int8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int q4_mmq_gemm_int8(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,

@@ -349,12 +349,13 @@ def test_mmq_2048_full(q4, orc, idx):
 
 
 def test_mmq_pp1024_gate_up(q4, orc):
-    # the prefill sweep's pp = 1024 point on the 4096 -> 12288 layer: 768
-    # tiles of 128 x 128, so the int8 design runs unsplit with 16 groups per
-    # tile (every other int8 test with more than two groups per tile splits K)
+    # the prefill sweep's pp = 1024 point on the 4096 -> 12288 layer: the
+    # routed call takes the int8 design here (384 tiles of 128 x 256, one and a
+    # half rounds of the CUs), the pipelined kernel with its per-row records
+    # in the workspace, 16 groups per tile
     c = wl.MMQ_2048[0]
     M = 1024
-    assert q4.q4_mmq_workspace_bytes(M, c["N"], c["K"]) == 0
+    assert q4.q4_mmq_workspace_bytes(M, c["N"], c["K"]) == q4.q4_mmq_int8_workspace_bytes(M, c["N"], c["K"]) > 0
     say("mmq pp1024 gate_up M=%d K=%d N=%d (every output)" % (M, c["K"], c["N"]))
     mmq_check(q4, orc, M, c["N"], c["K"], c["seed"], True, "mmq pp1024 gate_up")
 
