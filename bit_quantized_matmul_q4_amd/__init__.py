@@ -1,5 +1,6 @@
-"""MI355X (gfx950) 4-bit group-256 weight-quantized matmul: dequant-fused GEMV
-for decode and an int8-MFMA MMQ GEMM on Q8_1 activations for prefill.
+"""MI355X (gfx950) 4-bit group-256 weight-quantized matmul: a dequant-fused
+GEMV for decode (M = 1..16) and an MMQ GEMM on Q8_1 activations for prefill,
+with an integer design (exact i8 block dots) and an fp16 matrix-core design.
 
 The compute lives in libq4mi.so (HIP kernels behind the C ABI of
 include/q4mi.h); this package is the Python binding of that ABI.
