@@ -23,7 +23,9 @@ Algorithmic bytes of a GEMV: packed weights N*K/2 + scales N*K/256*4 + x M*K*4
 
 Both MMQ designs run in the step: q4_mmq_gemm as routed (the fp16 matrix-core
 design at these shapes) and q4_mmq_gemm_int8 (int8 matrix cores, exact int32
-block dots); each is reported against its own matrix-core peak.
+block dots); each is reported against its own matrix-core peak.  For context
+only, "vendor_gemm" times the vendor BLAS's plain GEMMs (torch.mm on fp16,
+torch._int_mm on int8 operands, no quantization scales) at the same shapes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --pmc-mmq        (Q8_1 + MMQ, M=2048 4096->12288, 3 launches;
@@ -320,6 +322,37 @@ def launch_floor_us(stream, n=252):
         for v in t:
             v.fill_(1.0)
     return round(graph_launch_us(run, n, stream), 3)
+
+
+def vendor_gemm(wl, dev, stream, reps=10):
+    """Context, not the library: the vendor BLAS's plain GEMMs (torch.mm on fp16
+    operands, torch._int_mm on int8 operands; no quantization scales) at the
+    MMQ prefill shapes, median of per-launch HIP-event times."""
+    import torch
+    out = {}
+    for c in [wl.MMQ_512] + list(wl.MMQ_2048):
+        M, K, N = c["M"], c["K"], c["N"]
+        g = torch.Generator(device=dev).manual_seed(0)
+        a = torch.randn((M, K), generator=g, device=dev).to(torch.float16)
+        b = torch.randn((K, N), generator=g, device=dev).to(torch.float16)  # contiguous K x N
+        ai = torch.randint(-127, 128, (M, K), generator=g, device=dev, dtype=torch.int8)
+        bi = torch.randint(-8, 8, (K, N), generator=g, device=dev, dtype=torch.int8)
+        res = {}
+        for name, fn in (("f16_mm", lambda: torch.mm(a, b)), ("i8_int_mm", lambda: torch._int_mm(ai, bi))):
+            for _ in range(3):
+                fn()
+            ev = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+            us = sorted(x.elapsed_time(y) for x, y in ev)[reps // 2] * 1e3
+            res[name] = {"us": round(us, 2), "tops": round(2.0 * M * N * K / us / 1e6, 1)}
+        out["M%d_K%d_N%d" % (M, K, N)] = res
+    return out
 
 
 def prefill_sweep(q4, wl, dev, stream):
@@ -684,6 +717,7 @@ def main():
     if not args.no_prefill_sweep:
         out["prefill_sweep"] = prefill_sweep(q4, wl, dev, stream)
     out["group32"] = group32_figures(q4, wl, dev, stream)
+    out["vendor_gemm"] = vendor_gemm(wl, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
