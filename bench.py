@@ -59,10 +59,11 @@ def mmq_bytes(M, N, K):
     return N * K // 2 + N * (K // 256) * 4 + M * K + M * (K // 32) * 4 + M * N * 4
 
 
-def f16_image_bytes(M, K):
-    """Workspace of q4_mmq_gemm's fp16 design: the fp16 activation image and row factors."""
+def f16_workspace_bytes(M, N, K):
+    """Workspace of q4_mmq_gemm's fp16 design: the fp16 activation image, row
+    factors and the weight rows' exponents."""
     rows = (M + 255) // 256 * 256
-    return rows * K * 2 + rows * 4
+    return rows * K * 2 + rows * 4 + (N + 127) // 128 * 128 * 8
 
 
 def q8_bytes(M, K):
@@ -634,7 +635,7 @@ def main():
         mmq_rep["M%d_%s" % (c["M"], c["name"])] = {
             "M": c["M"], "K": c["K"], "N": c["N"],
             "mmq_us": round(g_ms * 1e3, 2), "tops": round(ops / (g_ms * 1e-3) / 1e12, 2),
-            "design": "fp16" if q4.q4_mmq_workspace_bytes(c["M"], c["N"], c["K"]) == f16_image_bytes(c["M"], c["K"])
+            "design": "fp16" if q4.q4_mmq_workspace_bytes(c["M"], c["N"], c["K"]) == f16_workspace_bytes(c["M"], c["N"], c["K"])
                       else "int8",
             "frac_i8_peak": round(ops / (g_ms * 1e-3) / 1e12 / I8_PEAK_TOPS, 4),
             "frac_f16_peak": round(ops / (g_ms * 1e-3) / 1e12 / F16_PEAK_TFLOPS, 4),

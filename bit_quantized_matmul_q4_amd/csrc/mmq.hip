@@ -656,7 +656,7 @@ size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)
         }
     }
     if (mmq_uses_f16(M, N, K)) {
-        const size_t f = mmqf_workspace_bytes(M, K);
+        const size_t f = mmqf_workspace_bytes(M, N, K);
         if (f > need) need = f;
     }
     return need;
@@ -676,7 +676,7 @@ hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uin
                       const DeviceInfo &dev, hipStream_t stream)
 {
     if (mmq_uses_f16(M, N, K))
-        return launch_mmqf(qa, ds, M, qs, sm, N, K, false, y, nullptr, nullptr, workspace, stream);
+        return launch_mmqf(qa, ds, M, qs, sm, N, K, false, y, nullptr, nullptr, workspace, dev.num_cus, stream);
     return launch_mmq_int8(qa, ds, M, qs, sm, N, K, y, workspace, dev, stream);
 }
 
@@ -685,7 +685,7 @@ hipError_t launch_mmq_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const
                           const DeviceInfo &dev, hipStream_t stream)
 {
     if (mmq_uses_f16(M, N, K))
-        return launch_mmqf(qa, ds, M, qs, sm, N, K, true, y, nullptr, nullptr, workspace, stream);
+        return launch_mmqf(qa, ds, M, qs, sm, N, K, true, y, nullptr, nullptr, workspace, dev.num_cus, stream);
     return run_tiles(kOutY, true, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
                      dev.num_cus, stream);
 }
@@ -695,7 +695,7 @@ hipError_t launch_mmq_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, cons
                            void *workspace, const DeviceInfo &dev, hipStream_t stream)
 {
     if (mmq_uses_f16(M, N, K))
-        return launch_mmqf(qa, ds, M, qs, sm, N, K, false, nullptr, qo, dso, workspace, stream);
+        return launch_mmqf(qa, ds, M, qs, sm, N, K, false, nullptr, qo, dso, workspace, dev.num_cus, stream);
     return run_tiles(kOutQ8, false, qa, ds, M, qs, sm, N, K, nullptr, nullptr, qo, dso, workspace,
                      dev.num_cus, stream);
 }

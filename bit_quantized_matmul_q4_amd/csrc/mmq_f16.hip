@@ -110,6 +110,25 @@ __global__ __launch_bounds__(256) void k_mmqf_rowscale(const uint32_t *__restric
     if (lane == 0) fs[row] = row_factor(dm);
 }
 
+// Bound on a weight row's dequantized magnitudes from one (scale, minimum)
+// pair: |minimum| + 15 |scale|.
+__device__ __forceinline__ float pair_bound(uint32_t v)
+{
+    return fabsf(f16_bits_to_f32(v >> 16)) + 15.0f * fabsf(f16_bits_to_f32(v & 0xFFFFu));
+}
+
+// E[n] with 2^E * (the row's largest pair bound) in [2^-7, 2^-6), or 0 for
+// all-zero and non-finite rows.
+__device__ __forceinline__ int weight_exponent(float wmax)
+{
+    int e = 0;
+    if (wmax > 0.0f && wmax <= 3.0e38f) {
+        frexpf(wmax, &e);
+        return -6 - e;
+    }
+    return 0;
+}
+
 // The fp16 activation image of one (256-row tile mt, K step s): thread r
 // converts row mt * 256 + r, k in [64 s, 64 s + 64).  Vector (t, h, r) of the
 // step (t = 0..3 MFMA of the step, h = Q8_1 block of the step) holds
@@ -119,12 +138,31 @@ __global__ __launch_bounds__(256) void k_mmqf_rowscale(const uint32_t *__restric
 // block scales, loaded a round of 8 vectors at a time) and the step-0
 // workgroups store it for the GEMM's epilogue, in place of k_mmqf_rowscale;
 // taken when those repeated reads stay small (short K, few row tiles).
+// The last row of workgroups (blockIdx.y == tiles_m) instead finds each
+// weight row's exponent E (weight_exponent over its P pairs) for rows [0,
+// Np), Np = N rounded up to whole 128-row tiles: wexp[n] = (E, 2^-E as fp32
+// bits), (0, 1.0) past N.
 template <bool kRowScale>
 __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restrict__ qa,
                                                           const uint32_t *__restrict__ ds,
                                                           float *__restrict__ fs, int M, int K,
-                                                          uint4 *__restrict__ img)
+                                                          uint4 *__restrict__ img,
+                                                          const uint32_t *__restrict__ sm, int N, int P,
+                                                          int Np, int2 *__restrict__ wexp)
 {
+    if ((int)blockIdx.y == (int)gridDim.y - 1) {
+        const int stride = (int)gridDim.x * kFThreads;
+        for (int n = (int)blockIdx.x * kFThreads + (int)threadIdx.x; n < Np; n += stride) {
+            float wmax = 0.0f;
+            if (n < N) {
+                const uint32_t *row = sm + (int64_t)n * P;
+                for (int i = 0; i < P; ++i) wmax = fmaxf(wmax, pair_bound(row[i]));
+            }
+            const int e = n < N ? weight_exponent(wmax) : 0;
+            wexp[n] = make_int2(e, __float_as_int(ldexpf(1.0f, -e)));
+        }
+        return;
+    }
     const int s = blockIdx.x, mt = blockIdx.y, r = threadIdx.x;
     const int S = K / kFk;
     const int m = mt * kFm + r;
@@ -180,128 +218,109 @@ __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restri
 }
 
 // y (row stride ldy) for activation rows [0, M) and weight rows [0, N) of
-// this sub-problem; img/fs are its activation image and row factors.
-// Output modes: fp32 y, or y quantized to Q8_1 along n (qo int8 [M][ldy],
-// dso [M][ldy/32]) as q8_1_quantize would do it.  kG32: group-32 weights,
-// one (scale, minimum) pair per Q8_1 block; the pairs of a step travel with
-// it and the operand constants change per step.
+// this sub-problem; img/fs are its activation image and row factors, wexp
+// its weight rows' exponents.  Output modes: fp32 y, or y quantized to Q8_1
+// along n (qo int8 [M][ldy], dso [M][ldy/32]) as q8_1_quantize would do it.
+// kG32: group-32 weights, one (scale, minimum) pair per Q8_1 block; the pairs
+// of a step travel with it and the operand constants change per step.
 //
 // 512 threads = 8 waves, two per SIMD.  Waves 4-7 (one per SIMD) only load
 // K steps into LDS; waves 0-3 (one per SIMD) only compute, wave (wm, wn)
 // owning activation rows 128 wm .. 128 wm + 127 (four MFMA tiles) x weight
 // rows 64 wn .. 64 wn + 63 (two) over whole K steps (4 MFMA rounds per
-// step), so the computing waves never issue a vector-memory instruction.
+// step).  Workgroups are persistent: workgroup b takes tiles b, b + grid,
+// b + 2 grid, ... (through the XCD mapping), and the K steps of its tiles
+// form one stream: the loading waves run into the next tile's steps while
+// the computing waves write the last tile's outputs, whose stores drain
+// while the next tile computes.
 template <int kMode, bool kG32 = false>
 __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     const uint4 *__restrict__ img, uint32_t img_bytes, const float *__restrict__ fs,
-    const uint8_t *__restrict__ qs, const uint32_t *__restrict__ sm, float *__restrict__ y,
-    int8_t *__restrict__ qo, uint32_t *__restrict__ dso, int M, int N, int K, int tiles_m, int64_t ldy,
-    int vec_store)
+    const uint8_t *__restrict__ qs, const uint32_t *__restrict__ sm, const int2 *__restrict__ wexp,
+    float *__restrict__ y, int8_t *__restrict__ qo, uint32_t *__restrict__ dso, int M, int N, int K,
+    int tiles_m, int ntiles, int64_t ldy, int vec_store)
 {
     constexpr int kSV = stage_vecs(kG32);
     __shared__ int4_t lds[kStages * kSV];
     __shared__ uint32_t sSM[2][kFn];
-    __shared__ float sScale[kFn];
-    __shared__ int sE[kFn];
+    __shared__ int2 sWE[2][kFn];  // (E, 2^-E) of the weight rows of tiles with even / odd index
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool consumer = wave < 4;
     const int wn = wave & 1, wm = (wave >> 1) & 1, pw = wave - 4;
     const int l32 = lane & 31, h = lane >> 5;
-    const int tile = xcd_tile_f(blockIdx.x, gridDim.x);
-    const int mt = tile % tiles_m, nt = tile / tiles_m;
-    const int n0 = nt * kFn, m0 = mt * kFm;
     const int S = K / kFk, G = K / kGroup;
     const int P = kG32 ? K / kBlock : G;
+    // this workgroup's tiles: k = 0 .. nk-1; global step u = k S + s
+    const int nk = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int U = nk * S;
+    auto tile_of = [&](int k) { return xcd_tile_f((int)blockIdx.x + k * (int)gridDim.x, ntiles); };
     const uint32_t rowq = (uint32_t)K / 2;
+    const int Np = (N + kFn - 1) / kFn * kFn;
     const rsrc_t r_img = make_rsrc(img, img_bytes);
     const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowq);
     const rsrc_t r_sm = make_rsrc(sm, (uint32_t)N * P * 4u);
-    uint32_t nrow[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) nrow[j] = (uint32_t)(n0 + wn * 64 + 32 * j + l32);
-
-    auto pair_bound = [](uint32_t v) {
-        return fabsf(f16_bits_to_f32(v >> 16)) + 15.0f * fabsf(f16_bits_to_f32(v & 0xFFFFu));
-    };
-    auto exponent_of = [](float wmax) {
-        int e = 0;
-        if (wmax > 0.0f && wmax <= 3.0e38f) {
-            frexpf(wmax, &e);
-            return -6 - e;
-        }
-        return 0;
-    };
-    int E[2] = {0, 0};
-    if (kG32) {
-        const int r = tid >> 2, q = tid & 3;
-        const uint32_t base = (uint32_t)(n0 + r) * (uint32_t)P * 4u;
-        float wmax = 0.0f;
-        for (int i = q; 4 * i < P; i += 4) {
-            const uint4 v = buf_load16(r_sm, base + 16u * (uint32_t)i);
-            wmax = fmaxf(fmaxf(wmax, fmaxf(pair_bound(v.x), pair_bound(v.y))), fmaxf(pair_bound(v.z), pair_bound(v.w)));
-        }
-        wmax = fmaxf(wmax, dpp_f32<kDppQuadSwap1>(wmax));
-        wmax = fmaxf(wmax, dpp_f32<kDppQuadSwap2>(wmax));
-        if (q == 0) {
-            const int e = exponent_of(wmax);
-            sE[r] = e;
-            sScale[r] = ldexpf(1.0f, -e);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 2; ++j) E[j] = sE[wn * 64 + 32 * j + l32];
-    } else if (consumer) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            float wmax = 0.0f;
-            for (int g = h; g < G; g += 2) wmax = fmaxf(wmax, pair_bound(buf_load4(r_sm, (nrow[j] * G + g) * 4u)));
-            wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
-            E[j] = exponent_of(wmax);
-            if (h == 0 && wm == 0) sScale[wn * 64 + 32 * j + l32] = ldexpf(1.0f, -E[j]);
-        }
-    }
+    const rsrc_t r_we = make_rsrc(wexp, (uint32_t)Np * 8u);
 
     const uint32_t lds0 = lds_addr(lds);
     const uint32_t sm0 = lds_addr(&sSM[0][0]);
+    const uint32_t we0 = lds_addr(&sWE[0][0]);
 
     if (!consumer) {
-        // ---- producer: step s in stage s % kStages; 8 image pieces (2048
+        // ---- producer: step u in stage u % kStages; 8 image pieces (2048
         // vectors / 4 producers), one weight piece, with group-32 weights one
-        // piece of pairs: at least 9 loads per step.  Barrier B_s (the
-        // consumers' barrier between rounds 2 and 3 of step s) needs step
-        // s + 1 in LDS; after it, step s + kStages - 1 goes into the stage of
-        // step s - 1, whose reads the consumers finished before B_s. ----
+        // piece of pairs: at least 9 loads per step.  Barrier B_u (the
+        // consumers' barrier between rounds 2 and 3 of step u) needs step
+        // u + 1 in LDS; after it, step u + kStages - 1 goes into the stage of
+        // step u - 1, whose reads the consumers finished before B_u.  Steps
+        // past the last read the last step again (uniform load counts). ----
         const uint32_t wcol = (uint32_t)((pw * 64 + lane) & 127), wblk = (uint32_t)((pw * 64 + lane) >> 7);
-        const uint32_t wts_v = (n0 + wcol) * rowq + wblk * 16u;
-        const uint32_t sm32_v = (n0 + wcol) * (uint32_t)P * 4u + wblk * 4u;
-        auto issue = [&](int s) {
-            const int sl = min(s, S - 1);
-            const uint32_t stage = lds0 + (uint32_t)((s % kStages) * kSV) * 16u;
+        auto issue = [&](int u) {
+            const int ul = min(u, U - 1);
+            const int tile = tile_of(ul / S), sl = ul % S;
+            const int mt = tile % tiles_m, n0 = (tile / tiles_m) * kFn;
+            const uint32_t stage = lds0 + (uint32_t)((u % kStages) * kSV) * 16u;
             const uint32_t goff = (uint32_t)((mt * S + sl) * kStepVecs) * 16u;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t v = (uint32_t)(pw * 512 + i * 64);
                 dma16(r_img, (v + lane) * 16u, goff, stage + v * 16u);
             }
-            dma16(r_qs, wts_v, (uint32_t)sl * 32u, stage + (uint32_t)(kStepVecs + pw * 64) * 16u);
-            if (kG32) dma4(r_sm, sm32_v, (uint32_t)sl * 8u, stage + (uint32_t)(kStageVecs * 16 + pw * 256));
+            dma16(r_qs, ((uint32_t)n0 + wcol) * rowq + wblk * 16u, (uint32_t)sl * 32u,
+                  stage + (uint32_t)(kStepVecs + pw * 64) * 16u);
+            if (kG32)
+                dma4(r_sm, ((uint32_t)n0 + wcol) * (uint32_t)P * 4u + wblk * 4u, (uint32_t)sl * 8u,
+                     stage + (uint32_t)(kStageVecs * 16 + pw * 256));
         };
-        auto issue_sm = [&](int g) {
-            if (!kG32 && pw < 2 && g < G) {
+        // group gg of the stream (tile gg / G, group gg % G): its pairs into sSM[gg & 1]
+        auto issue_sm = [&](int gg) {
+            if (!kG32 && pw < 2 && gg < nk * G) {
+                const int n0 = (tile_of(gg / G) / tiles_m) * kFn;
                 const uint32_t c = (uint32_t)(pw * 64 + lane);
-                dma4(r_sm, (n0 + c) * G * 4u, (uint32_t)g * 4u, sm0 + (uint32_t)((g & 1) * kFn + pw * 64) * 4u);
+                dma4(r_sm, ((uint32_t)n0 + c) * (uint32_t)G * 4u, (uint32_t)(gg % G) * 4u,
+                     sm0 + (uint32_t)((gg & 1) * kFn + pw * 64) * 4u);
             }
         };
+        // tile k's weight-row exponents into sWE[k & 1] (1 KB, one load per lane of wave 6)
+        auto issue_we = [&](int k) {
+            if (pw == 2 && k < nk) {
+                const int n0 = (tile_of(k) / tiles_m) * kFn;
+                dma16(r_we, (uint32_t)n0 * 8u + (uint32_t)lane * 16u, 0u, we0 + (uint32_t)((k & 1) * kFn * 8));
+            }
+        };
+        issue_we(0);
         issue_sm(0);
-        for (int s = 0; s < kStages - 2; ++s) issue(s);
-        wait_vm_barrier<9 * (kStages - 3)>();  // B_init: step 0
+        for (int u = 0; u < kStages - 2; ++u) issue(u);
+        wait_vm_barrier<9 * (kStages - 3)>();  // B_init: step 0, its pairs and exponents
         issue(kStages - 2);
-        for (int s = 0; s < S; ++s) {
-            wait_vm_barrier<9 * (kStages - 3)>();  // B_s: step s + 1
-            issue(s + kStages - 1);
-            if ((s & 3) == 0) issue_sm((s >> 2) + 1);
+        for (int u = 0; u < U; ++u) {
+            wait_vm_barrier<9 * (kStages - 3)>();  // B_u: step u + 1
+            issue(u + kStages - 1);
+            if ((u & 3) == 0) issue_sm((u >> 2) + 1);
+            // from B_{k S} on the consumers are past tile k - 1's epilogue,
+            // the last reader of sWE[(k + 1) & 1]
+            if (u % S == 0) issue_we(u / S + 1);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         return;
@@ -309,32 +328,38 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
 
     // ---- consumer ----
     float16_t acc[2][4];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
-    auto read_frags = [&](int s, int t, f16x8 (&bv)[4]) {
-        const int4_t *act = lds + (s % kStages) * kSV + wm * 128 + l32;
+                for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+    };
+    zero_acc();
+    auto read_frags = [&](int u, int t, f16x8 (&bv)[4]) {
+        const int4_t *act = lds + (u % kStages) * kSV + wm * 128 + l32;
 #pragma unroll
         for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(f16x8, act[(2 * t + h) * kFm + 32 * i]);
     };
-    auto read_wts = [&](int s, int4_t (&wq)[2]) {
-        const int4_t *wv = lds + (s % kStages) * kSV + kStepVecs + h * kFn + wn * 64 + l32;
+    auto read_wts = [&](int u, int4_t (&wq)[2]) {
+        const int4_t *wv = lds + (u % kStages) * kSV + kStepVecs + h * kFn + wn * 64 + l32;
 #pragma unroll
         for (int j = 0; j < 2; ++j) wq[j] = wv[32 * j];
     };
     half2_t cs[2], cs16[2], cmn[2];
-    auto consts = [&](int s) {
-        // group 256: the constants of step s's group; group 32: of step s
-        const uint32_t *sm32 = reinterpret_cast<const uint32_t *>(lds + (s % kStages) * kSV + kStageVecs);
+    auto consts = [&](int u) {
+        // group 256: the constants of step u's group; group 32: of step u
+        const uint32_t *sm32 = reinterpret_cast<const uint32_t *>(lds + (u % kStages) * kSV + kStageVecs);
+        const int2 *we = sWE[(u / S) & 1];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint32_t w = kG32 ? sm32[h * kFn + wn * 64 + 32 * j + l32] : sSM[(s >> 2) & 1][wn * 64 + 32 * j + l32];
+            const int r = wn * 64 + 32 * j + l32;
+            const uint32_t w = kG32 ? sm32[h * kFn + r] : sSM[(u >> 2) & 1][r];
+            const int E = we[r].x;
             const float sc = f16_bits_to_f32(w & 0xFFFFu), mn = f16_bits_to_f32(w >> 16);
-            const _Float16 a = (_Float16)ldexpf(sc, E[j] + 24), b = (_Float16)ldexpf(sc, E[j] + 20),
-                           c = (_Float16)ldexpf(mn, E[j]);
+            const _Float16 a = (_Float16)ldexpf(sc, E + 24), b = (_Float16)ldexpf(sc, E + 20),
+                           c = (_Float16)ldexpf(mn, E);
             cs[j] = half2_t{a, a};
             cs16[j] = half2_t{b, b};
             cmn[j] = half2_t{c, c};
@@ -358,13 +383,90 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
             for (int i = 0; i < 4; ++i)
                 acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[j], bv[i], acc[j][i], 0, 0, 0);
     };
+    // the row factors of tile k's activation rows, loaded when the tile
+    // starts and used by its epilogue
+    float fin[4];
+    auto load_factors = [&](int k) {
+        const int m0 = (tile_of(k) % tiles_m) * kFm;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wm * 128 + 32 * i + l32;
+            fin[i] = m < M ? fs[m] : 1.0f;
+        }
+    };
+    // tile k's outputs from acc: y[m][n] = acc * 2^-E[n] / F[m]
+    auto epilogue = [&](int k) {
+        const int tile = tile_of(k);
+        const int m0 = (tile % tiles_m) * kFm, n0 = (tile / tiles_m) * kFn;
+        const int2 *we = sWE[k & 1];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int nl = wn * 64 + 32 * j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + wm * 128 + 32 * i + l32;
+                const float fi = m < M ? 1.0f / fin[i] : 0.0f;
+                const float16_t &a = acc[j][i];
+                float v[16];
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        v[4 * r4 + c] = a[4 * r4 + c] * fi * __int_as_float(we[nl + 8 * r4 + 4 * h + c].y);
+                }
+                if (kMode == kFOutQ8) {
+                    const int nb = n0 + nl;
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+                    amax = fmaxf(amax, __shfl_xor(amax, 32));
+                    const uint16_t d16 = q8_1_scale(amax);
+                    const float df = f16_bits_to_f32(d16);
+                    int sum = 0;
+                    uint32_t packed[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        packed[q] = 0;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int c = q8_1_code(v[4 * q + r], df);
+                            sum += c;
+                            packed[q] |= ((uint32_t)c & 0xFFu) << (8 * r);
+                        }
+                    }
+                    sum += __shfl_xor(sum, 32);
+                    if (m < M && nb < N) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<uint32_t *>(qo + (int64_t)m * ldy + nb + 8 * q + 4 * h) = packed[q];
+                        if (h == 0) dso[(int64_t)m * (ldy / kBlock) + nb / kBlock] = q8_1_ds(d16, df, sum);
+                    }
+                } else if (m < M) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int n = n0 + nl + 8 * r4 + 4 * h;
+                        float *dst = y + (int64_t)m * ldy + n;
+                        if (vec_store && n + 3 < N) {
+                            *reinterpret_cast<float4 *>(dst) =
+                                make_float4(v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]);
+                        } else {
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)
+                                if (n + c < N) dst[c] = v[4 * r4 + c];
+                        }
+                    }
+                }
+            }
+        }
+    };
 
     // Each round's fragments and weights are read and unpacked during the
     // round before: one scheduling region holds a round's 8 MFMAs and the
     // next round's LDS reads and unpack, interleaved one MFMA, one read and
-    // three VALU ops at a time so the VALU runs in the MFMAs' shadow.  B_s
-    // falls between rounds 2 and 3, and step s + 1's first operands are read
-    // after it, during round 3.
+    // three VALU ops at a time so the VALU runs in the MFMAs' shadow.  B_u
+    // falls between rounds 2 and 3, and step u + 1's first operands are read
+    // after it, during round 3 (the next tile's first step after a tile's
+    // last).
     auto interleave = [&]() {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -373,7 +475,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
         }
     };
-    wait_vm_barrier<63>();  // B_init (consumers issue no loads: no wait)
+    load_factors(0);
+    wait_vm_barrier<63>();  // B_init (consumers wait for no loads of their own)
     f16x8 bv0[4], bv1[4], av0[2], av1[2];
     int4_t wq[2];
     read_wts(0, wq);
@@ -381,94 +484,41 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     read_frags(0, 0, bv0);
     unpack(0, wq, av0);
 #pragma unroll 1
-    for (int s = 0; s < S; ++s) {
+    for (int u = 0; u < U; ++u) {
         __builtin_amdgcn_sched_barrier(0);
         mfmas(av0, bv0);                       // round 0
-        read_frags(s, 1, bv1);
+        read_frags(u, 1, bv1);
         unpack(1, wq, av1);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
         mfmas(av1, bv1);                       // round 1
-        read_frags(s, 2, bv0);
+        read_frags(u, 2, bv0);
         unpack(2, wq, av0);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
         mfmas(av0, bv0);                       // round 2
-        read_frags(s, 3, bv1);
+        read_frags(u, 3, bv1);
         unpack(3, wq, av1);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm_barrier<63>();                 // B_s: step s + 1 in LDS
+        wait_vm_barrier<63>();                 // B_u: step u + 1 in LDS
         int4_t wqn[2];
-        read_wts(s + 1, wqn);
-        if (kG32 || ((s + 1) & 3) == 0) consts(s + 1);
+        read_wts(u + 1, wqn);
+        if (kG32 || ((u + 1) & 3) == 0) consts(u + 1);
         mfmas(av1, bv1);                       // round 3
-        read_frags(s + 1, 0, bv0);
+        read_frags(u + 1, 0, bv0);
         unpack(0, wqn, av0);
         interleave();
         wq[0] = wqn[0];
         wq[1] = wqn[1];
-    }
-
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int nl = wn * 64 + 32 * j;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + wm * 128 + 32 * i + l32;
-            const float fi = m < M ? 1.0f / fs[m] : 0.0f;
-            const float16_t &a = acc[j][i];
-            float v[16];
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 sc = *reinterpret_cast<const float4 *>(sScale + nl + 8 * r4 + 4 * h);
-                v[4 * r4] = a[4 * r4] * fi * sc.x;
-                v[4 * r4 + 1] = a[4 * r4 + 1] * fi * sc.y;
-                v[4 * r4 + 2] = a[4 * r4 + 2] * fi * sc.z;
-                v[4 * r4 + 3] = a[4 * r4 + 3] * fi * sc.w;
-            }
-            if (kMode == kFOutQ8) {
-                const int nb = n0 + nl;
-                float amax = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
-                amax = fmaxf(amax, __shfl_xor(amax, 32));
-                const uint16_t d16 = q8_1_scale(amax);
-                const float df = f16_bits_to_f32(d16);
-                int sum = 0;
-                uint32_t packed[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    packed[q] = 0;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int c = q8_1_code(v[4 * q + r], df);
-                        sum += c;
-                        packed[q] |= ((uint32_t)c & 0xFFu) << (8 * r);
-                    }
-                }
-                sum += __shfl_xor(sum, 32);
-                if (m < M && nb < N) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<uint32_t *>(qo + (int64_t)m * ldy + nb + 8 * q + 4 * h) = packed[q];
-                    if (h == 0) dso[(int64_t)m * (ldy / kBlock) + nb / kBlock] = q8_1_ds(d16, df, sum);
-                }
-            } else if (m < M) {
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int n = n0 + nl + 8 * r4 + 4 * h;
-                    float *dst = y + (int64_t)m * ldy + n;
-                    if (vec_store && n + 3 < N) {
-                        *reinterpret_cast<float4 *>(dst) =
-                            make_float4(v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            if (n + c < N) dst[c] = v[4 * r4 + c];
-                    }
-                }
-            }
+        if ((u + 1) % S == 0) {
+            // tile u / S is complete: its outputs go out while the loading
+            // waves already fill the next tile's steps
+            __builtin_amdgcn_sched_barrier(0);
+            const int k = u / S;
+            epilogue(k);
+            zero_acc();
+            if (k + 1 < nk) load_factors(k + 1);
         }
     }
 }
@@ -489,23 +539,28 @@ int64_t chunk_rows(int64_t M, int64_t K)
 
 }  // namespace
 
-size_t mmqf_workspace_bytes(int64_t M, int64_t K)
+// [image: rows x K fp16][row factors: rows fp32][weight-row (E, 2^-E): N
+// rounded up to whole tiles]
+size_t mmqf_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    if (M < 1 || K < kGroup) return 0;
+    if (M < 1 || N < 1 || K < kGroup) return 0;
     const int64_t rows = chunk_rows(M, K);
-    return (size_t)(rows * K * 2 + rows * (int64_t)sizeof(float));
+    return (size_t)(rows * K * 2 + rows * (int64_t)sizeof(float) + round_up(N, kFn) * (int64_t)sizeof(int2));
 }
 
 hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                        const uint16_t *sm, int64_t N, int K, bool g32, float *y, int8_t *qo, uint16_t *dso,
-                       void *workspace, hipStream_t stream)
+                       void *workspace, int num_cus, hipStream_t stream)
 {
     const int B = K / kBlock, S = K / kFk;
     const int P = g32 ? B : K / kGroup;  // (scale, minimum) pairs per weight row
     if (g32 && !y) return hipErrorInvalidValue;  // group 32: fp32 output only
     const int64_t rows_max = chunk_rows(M, K);
+    const int64_t npad = round_up(N, kFn);
+    if (npad > 0x7FFFFFFF) return hipErrorInvalidValue;
     uint4 *img = static_cast<uint4 *>(workspace);
     float *fs = reinterpret_cast<float *>(static_cast<char *>(workspace) + rows_max * K * 2);
+    int2 *wexp = reinterpret_cast<int2 *>(static_cast<char *>(workspace) + rows_max * K * 2 + rows_max * 4);
     const uint32_t *ds32 = reinterpret_cast<const uint32_t *>(ds);
     const uint32_t *sm32 = reinterpret_cast<const uint32_t *>(sm);
     uint32_t *dso32 = reinterpret_cast<uint32_t *>(dso);
@@ -521,31 +576,36 @@ hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const ui
         // stay within kFusedScaleBytes and the scales allow 16-byte loads;
         // otherwise a separate pass
         if (mp * S * B * 4 <= kFusedScaleBytes && (reinterpret_cast<uintptr_t>(ds) & 15) == 0) {
-            hipLaunchKernelGGL(k_mmqf_image<true>, dim3((unsigned)S, (unsigned)tiles_m), dim3(kFThreads), 0,
-                               stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm, K, img);
+            hipLaunchKernelGGL(k_mmqf_image<true>, dim3((unsigned)S, (unsigned)(tiles_m + 1)), dim3(kFThreads), 0,
+                               stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm, K, img, sm32, (int)N, P,
+                               (int)npad, wexp);
         } else {
             hipLaunchKernelGGL(k_mmqf_rowscale, dim3((unsigned)(mp / 4)), dim3(256), 0, stream, ds32 + m0 * B,
                                (int)mm, B, (int)mp, fs);
-            hipLaunchKernelGGL(k_mmqf_image<false>, dim3((unsigned)S, (unsigned)tiles_m), dim3(kFThreads), 0,
-                               stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm, K, img);
+            hipLaunchKernelGGL(k_mmqf_image<false>, dim3((unsigned)S, (unsigned)(tiles_m + 1)), dim3(kFThreads), 0,
+                               stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm, K, img, sm32, (int)N, P,
+                               (int)npad, wexp);
         }
         for (int64_t n0 = 0; n0 < N; n0 += n_max) {
             const int64_t nn = N - n0 < n_max ? N - n0 : n_max;
             const int64_t tiles = (int64_t)tiles_m * ((nn + kFn - 1) / kFn);
             if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+            // persistent: one workgroup per CU (the LDS of one), each taking
+            // every grid-th tile
+            const unsigned grid = (unsigned)(tiles < num_cus ? tiles : num_cus);
             if (y) {
                 float *y0 = y + m0 * N + n0;
                 const int vec_store = (N % 4 == 0) && (nn % 4 == 0) &&
                                       ((reinterpret_cast<uintptr_t>(y0) & 15) == 0);
                 auto kern = g32 ? k_mmqf<kFOutY, true> : k_mmqf<kFOutY, false>;
-                hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, img, img_bytes, fs,
-                                   qs + n0 * (K / 2), sm32 + n0 * P, y0, (int8_t *)nullptr, (uint32_t *)nullptr,
-                                   (int)mm, (int)nn, K, tiles_m, N, vec_store);
+                hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), 0, stream, img, img_bytes, fs,
+                                   qs + n0 * (K / 2), sm32 + n0 * P, wexp + n0, y0, (int8_t *)nullptr,
+                                   (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, (int)tiles, N, vec_store);
             } else {
-                hipLaunchKernelGGL((k_mmqf<kFOutQ8, false>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream,
-                                   img, img_bytes, fs,
-                                   qs + n0 * (K / 2), sm32 + n0 * P, (float *)nullptr, qo + m0 * N + n0,
-                                   dso32 + m0 * (N / kBlock) + n0 / kBlock, (int)mm, (int)nn, K, tiles_m, N, 0);
+                hipLaunchKernelGGL((k_mmqf<kFOutQ8, false>), dim3(grid), dim3(kGemmThreads), 0, stream, img,
+                                   img_bytes, fs, qs + n0 * (K / 2), sm32 + n0 * P, wexp + n0, (float *)nullptr,
+                                   qo + m0 * N + n0, dso32 + m0 * (N / kBlock) + n0 / kBlock, (int)mm, (int)nn, K,
+                                   tiles_m, (int)tiles, N, 0);
             }
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;

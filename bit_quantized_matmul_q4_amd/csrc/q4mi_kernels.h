@@ -55,10 +55,10 @@ hipError_t launch_mmq_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, cons
                            void *workspace, const DeviceInfo &dev, hipStream_t stream);
 // fp16 matrix-core MMQ (mmq_f16.hip): y (fp32) or, with y null, Q8_1 output;
 // g32: group-32 weights (fp32 output only)
-size_t mmqf_workspace_bytes(int64_t M, int64_t K);
+size_t mmqf_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                        const uint16_t *sm, int64_t N, int K, bool g32, float *y, int8_t *qo, uint16_t *dso,
-                       void *workspace, hipStream_t stream);
+                       void *workspace, int num_cus, hipStream_t stream);
 hipError_t launch_block_dots(const int8_t *qa, int64_t M, const uint8_t *qs, int64_t N, int K,
                              int32_t *idot, const DeviceInfo &dev, hipStream_t stream);
 

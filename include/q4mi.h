@@ -203,8 +203,9 @@ int q4_mmq_gemm_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8
  * q4_mmq_workspace_bytes -- device workspace q4_mmq_gemm (and
  * q4_mmq_gemm_q8_1, q4_mmq_gemm_g32) needs for this shape: the fp16
  * activation image of the fp16 path (2 * K bytes per activation row, at
- * most 256 MiB + 2 * K * 256 bytes, plus 4 bytes per row), or what the int8
- * path needs (q4_mmq_int8_workspace_bytes).  Pure host function.  Returns 0
+ * most 256 MiB + 2 * K * 256 bytes, plus 4 bytes per row) and 8 bytes per
+ * weight row (N rounded up to 128), or what the int8 path needs
+ * (q4_mmq_int8_workspace_bytes).  Pure host function.  Returns 0
  * for shapes q4_mmq_gemm would reject.
  */
 size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);

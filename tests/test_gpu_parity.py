@@ -538,16 +538,18 @@ def test_mmq_degenerate_groups(q4, orc):
 # its workspace (the fp16 activation image, 2 K bytes per row padded to 256
 # rows, plus 4 bytes per row) tells which design a shape takes.
 
-def f16_workspace(M, K):
+def f16_workspace(M, N, K):
+    # activation image (2 K bytes per row, rows padded to 256), a row factor
+    # per row, and (E, 2^-E) per weight row (rows padded to 128)
     rows = (M + 255) // 256 * 256
-    return rows * K * 2 + rows * 4
+    return rows * K * 2 + rows * 4 + (N + 127) // 128 * 128 * 8
 
 
 def test_mmq_f16_ragged(q4, orc):
     # 2 x 100 tiles, both edges ragged (300 = 256 + 44 rows, 12700 = 99 * 128 + 28)
     M, N, K = 300, 12700, 512
     say("mmq fp16 design M=%d N=%d K=%d" % (M, N, K))
-    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, K)
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, N, K)
     mmq_check(q4, orc, M, N, K, 71, True, "mmq fp16 ragged")
 
 
@@ -557,7 +559,7 @@ def test_mmq_f16_extremes(q4, orc):
     # activation rows scaled by 1e-4 and 6e4 and weight rows by 1e-5 and 1e4
     M, N, K = 260, 12300, 1024
     say("mmq fp16 design with extreme and degenerate rows M=%d N=%d K=%d" % (M, N, K))
-    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, K)
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, N, K)
     rng = np.random.default_rng(14)
     x = rng.standard_normal((M, K)).astype(np.float32)
     x[0] = 0.0
@@ -596,7 +598,7 @@ def test_mmq_f16_extremes(q4, orc):
 def test_mmq_f16_q8_1_output_bit_exact(q4, orc):
     M, N, K = 300, 12288, 512
     say("mmq fp16 design -> Q8_1 M=%d N=%d K=%d" % (M, N, K))
-    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, K)
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, N, K)
     W, x = wl.mmq_case(72, M, N, K, True)
     qs, sm = q4.q4_pack(dev(W))
     qa, ds = q4.q8_1_quantize(dev(x))
@@ -614,7 +616,7 @@ def test_mmq_f16_q8_1_output_bit_exact(q4, orc):
 def test_mmq_f16_deterministic(q4, orc):
     M, N, K = 512, 9216, 2560
     say("mmq fp16 design rerun determinism M=%d N=%d K=%d" % (M, N, K))
-    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, K)
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, N, K)
     W, x = wl.mmq_case(73, M, N, K, True)
     qs, sm = q4.q4_pack(dev(W))
     qa, ds = q4.q8_1_quantize(dev(x))
