@@ -155,8 +155,17 @@ __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restri
         for (int n = (int)blockIdx.x * kFThreads + (int)threadIdx.x; n < Np; n += stride) {
             float wmax = 0.0f;
             if (n < N) {
+                // eight loads in flight at a time
                 const uint32_t *row = sm + (int64_t)n * P;
-                for (int i = 0; i < P; ++i) wmax = fmaxf(wmax, pair_bound(row[i]));
+                int i = 0;
+                for (; i + 8 <= P; i += 8) {
+                    uint32_t v[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[j] = row[i + j];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) wmax = fmaxf(wmax, pair_bound(v[j]));
+                }
+                for (; i < P; ++i) wmax = fmaxf(wmax, pair_bound(row[i]));
             }
             const int e = n < N ? weight_exponent(wmax) : 0;
             wexp[n] = make_int2(e, __float_as_int(ldexpf(1.0f, -e)));
