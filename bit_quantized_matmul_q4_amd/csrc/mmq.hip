@@ -617,8 +617,8 @@ bool mmq_uses_f16(int64_t M, int64_t N, int64_t K)
 }
 
 // The int8 design's fp32-output kernels: the pipelined k_mmqi (mmq_i8.hip,
-// 128 x 256 tiles, one workgroup per CU) when its grid covers at least half
-// the CUs, otherwise k_mmq here (128 x 128 tiles, two per CU, K split for
+// 128 x 128 tiles, one workgroup per CU) when its grid has at least one tile
+// per CU, otherwise k_mmq here (128 x 128 tiles, two per CU, K split for
 // small grids).  A function of the shape only.
 bool mmq_int8_pipelined(int64_t M, int64_t N, int64_t K)
 {
@@ -643,8 +643,9 @@ size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < kGroup) return 0;
     // the K-split partials of k_mmq (Q8_1 output and group-32 weights take it
-    // at any grid), the records of k_mmqi, the fp16 design's image
-    size_t need = mmq_int8_workspace_bytes(M, N, K);
+    // at any grid), what k_mmqi needs where the call routes to it, the fp16
+    // design's image
+    size_t need = mmq_uses_f16(M, N, K) ? 0 : mmq_int8_workspace_bytes(M, N, K);
     {
         const SplitCfg sc = choose_split(M, N, (int)K);
         if (sc.nsplit > 1) {
