@@ -69,11 +69,11 @@ def test_graph_replays_match_eager(q4):
     # the fp16 design's workspace holds its activation image (2 K bytes per
     # row, rows padded to 256, plus 4 bytes per row) and 8 bytes per weight
     # row, and covers the K-split partials of the Q8_1-output and group-32
-    # int8 kernels where those exceed it; q4_mmq_gemm_int8 has its own (byte
-    # planes and records)
+    # int8 kernels where those exceed it; q4_mmq_gemm_int8 has its own (the
+    # per-row and per-weight-row records of its pipelined kernel)
     assert q4.q4_mmq_workspace_bytes(300, 12288, 512) == 512 * (2 * 512 + 4) + 12288 * 8
     assert q4.q4_mmq_workspace_bytes(512, 8192, 4096) >= 512 * (2 * 4096 + 4) + 8192 * 8
-    assert q4.q4_mmq_int8_workspace_bytes(512, 8192, 4096) >= 3 * 512 * 4096
+    assert q4.q4_mmq_int8_workspace_bytes(512, 8192, 4096) == 512 * 16 * 32 + 8192 * 16 * 8
     # the shapes take the K-split paths (partials and a second, summing kernel)
     assert q4.q4_mmq_workspace_bytes(100, 224, 2048) > 0
     assert q4.q4_gemv_workspace_bytes(8, 512, 4096) > 0
