@@ -350,9 +350,10 @@ def test_mmq_2048_full(q4, orc, idx):
 
 def test_mmq_pp1024_gate_up(q4, orc):
     # the prefill sweep's pp = 1024 point on the 4096 -> 12288 layer: the
-    # routed call takes the int8 design here (384 tiles of 128 x 256, one and a
-    # half rounds of the CUs), the pipelined kernel with its per-row records
-    # in the workspace, 16 groups per tile
+    # routed call takes the int8 design here (the fp16 design's 384 tiles of
+    # 256 x 128 would be one and a half rounds of the CUs): the pipelined
+    # kernel, 768 tiles of 128 x 128 with its per-row records in the
+    # workspace, 16 groups per tile
     c = wl.MMQ_2048[0]
     M = 1024
     assert q4.q4_mmq_workspace_bytes(M, c["N"], c["K"]) == q4.q4_mmq_int8_workspace_bytes(M, c["N"], c["K"]) > 0
@@ -551,6 +552,25 @@ def test_mmq_f16_ragged(q4, orc):
     say("mmq fp16 design M=%d N=%d K=%d" % (M, N, K))
     assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, N, K)
     mmq_check(q4, orc, M, N, K, 71, True, "mmq fp16 ragged")
+
+
+def test_mmq_f16_persistent_uneven(q4, orc):
+    # 5 x 100 = 500 tiles over one workgroup per CU: most workgroups take two
+    # tiles (the second one's stages stream in behind the first one's
+    # epilogue), the rest one, and both edges are ragged (1100 = 4 * 256 +
+    # 76 rows, 12700 = 99 * 128 + 28); the Q8_1 output takes the same tiles
+    M, N, K = 1100, 12700, 512
+    say("mmq fp16 design, uneven persistent tiles M=%d N=%d K=%d" % (M, N, K))
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, N, K)
+    y = mmq_check(q4, orc, M, N, K, 75, True, "mmq fp16 persistent uneven")
+    N8 = 12672  # a multiple of 32 for the Q8_1 output, still ragged at 99 * 128
+    W, x = wl.mmq_case(76, M, N8, K, True)
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    qo, dso = q4.q4_mmq_gemm_q8_1(qa, ds, qs, sm)
+    qr, dsr = q4.q8_1_quantize(q4.q4_mmq_gemm(qa, ds, qs, sm))
+    torch.cuda.synchronize()
+    assert torch.equal(qo, qr) and torch.equal(dso.view(torch.int16), dsr.view(torch.int16))
 
 
 def test_mmq_f16_extremes(q4, orc):
