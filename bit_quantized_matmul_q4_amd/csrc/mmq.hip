@@ -50,6 +50,7 @@
 //     of LDS, so two workgroups share a CU and hide each other's staging.
 #include "q4mi_device.h"
 #include "q4mi_kernels.h"
+#include "mmq_tiles.h"
 
 namespace q4mi {
 
@@ -78,17 +79,6 @@ __host__ __device__ constexpr int mmq_lds_bytes(bool g32) { return g32 ? kLdsA +
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
-
-// Map the linear workgroup id so that the 8 XCDs (which receive workgroups
-// round-robin) each own a contiguous run of tiles.
-__device__ __forceinline__ int xcd_tile(int pid, int ntiles)
-{
-    constexpr int kXcd = 8;
-    const int per = ntiles / kXcd, rem = ntiles % kXcd;
-    const int xcd = pid % kXcd, local = pid / kXcd;
-    // the first rem XCDs own per + 1 tiles, the others per
-    return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-}
 
 // y and idot point at the sub-problem's first output; ldy / ldi are the row
 // strides (elements) of the full outputs.

@@ -45,10 +45,13 @@
 //   * The image is laid out per (256-row tile, K step) in LDS order: the
 //     loads are contiguous 1 KB per instruction and the LDS reads (16 bytes
 //     per lane, consecutive rows) are conflict-free.
-//   * Tiles are mapped so each XCD works on a contiguous run of tiles (m
-//     fastest), which keeps the shared activation and weight tiles in its L2.
+//   * Tiles are mapped so each XCD works on a contiguous run of tiles in
+//     groups of few activation-row tiles (m fastest within a group), which
+//     keeps the shared activation and weight tiles in its L2 and reads each
+//     XCD's activation slice and each weight tile once.
 #include "q4mi_device.h"
 #include "q4mi_kernels.h"
+#include "mmq_tiles.h"
 
 namespace q4mi {
 
@@ -72,14 +75,6 @@ constexpr int64_t kImageMaxBytes = (int64_t)256 << 20;
 enum { kFOutY = 0, kFOutQ8 = 1 };
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ int xcd_tile_f(int pid, int ntiles)
-{
-    constexpr int kXcd = 8;
-    const int per = ntiles / kXcd, rem = ntiles % kXcd;
-    const int xcd = pid % kXcd, local = pid / kXcd;
-    return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-}
 
 // F[r] for rows r < rows: 2^(8 - e) with e the binary exponent of the row's
 // largest block scale (d = f * 2^e, f in [0.5, 1)), so 127 * d * F < 2^15;
@@ -264,7 +259,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     // this workgroup's tiles: k = 0 .. nk-1; global step u = k S + s
     const int nk = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int U = nk * S;
-    auto tile_of = [&](int k) { return xcd_tile_f((int)blockIdx.x + k * (int)gridDim.x, ntiles); };
+    // each XCD runs a contiguous stretch of tiles in grouped order (about one
+    // 256-row image slice against many weight tiles, so each XCD reads its
+    // image slice and each weight tile once), returned as the m-fastest index
+    // the rest uses
+    auto tile_of = [&](int k) {
+        int mt, nt;
+        grouped_tile(xcd_tile((int)blockIdx.x + k * (int)gridDim.x, ntiles), tiles_m, ntiles / tiles_m, mt, nt);
+        return mt + nt * tiles_m;
+    };
     const uint32_t rowq = (uint32_t)K / 2;
     const int Np = (N + kFn - 1) / kFn * kFn;
     const rsrc_t r_img = make_rsrc(img, img_bytes);

@@ -43,6 +43,7 @@
 
 #include "q4mi_device.h"
 #include "q4mi_kernels.h"
+#include "mmq_tiles.h"
 
 namespace q4mi {
 
@@ -79,14 +80,6 @@ __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 256
 // XOR-swizzled by bit 3 of the row so that sixteen consecutive rows at one
 // chunk cover all 64 banks once
 __device__ __forceinline__ uint32_t recoff(uint32_t r, uint32_t c) { return r * 32u + 16u * (c ^ ((r >> 3) & 1u)); }
-
-__device__ __forceinline__ int xcd_tile_i(int pid, int ntiles)
-{
-    constexpr int kXcd = 8;
-    const int per = ntiles / kXcd, rem = ntiles % kXcd;
-    const int xcd = pid % kXcd, local = pid / kXcd;
-    return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-}
 
 // Blocks [0, rowblocks): eight lanes per (activation row m, group g), lane b
 // taking block b, records [g][Mp] of kRecBytes (rows >= M are zeros: their
@@ -170,8 +163,11 @@ __global__ __launch_bounds__(kPThreads, 2) void k_mmqi(const int8_t *__restrict_
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave & 1, wm = wave >> 1;
     const int l32 = lane & 31, half = lane >> 5;
-    const int tile = xcd_tile_i(blockIdx.x, gridDim.x);
-    const int mt = tile % tiles_m, nt = tile / tiles_m;
+    // each XCD runs a contiguous stretch of tiles in grouped order: its one
+    // or two 128-row activation tiles against every weight tile, each read
+    // once per XCD
+    int mt, nt;
+    grouped_tile(xcd_tile(blockIdx.x, gridDim.x), tiles_m, (int)gridDim.x / tiles_m, mt, nt);
     const int m0 = mt * kPm, n0 = nt * kPn;
     const int G = K / kGroup;
     const uint32_t rowq = (uint32_t)K / 2;
