@@ -377,7 +377,7 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
             for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(yacc[ta][e]));
             amax = fmaxf(amax, __shfl_xor(amax, 32));
             const uint16_t d16 = q8_1_scale(amax);
-            const float df = f16_bits_to_f32(d16);
+            const float df = f16_bits_to_f32(d16), rdf = q8_1_rcp(df);
             int sum = 0;
             uint32_t packed[4];
 #pragma unroll
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(512, kMode == kOutDots ? 1 : 4) void k_mmq(
                 packed[q] = 0;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int a = q8_1_code(yacc[ta][4 * q + r], df);
+                    const int a = q8_1_code(yacc[ta][4 * q + r], df, rdf);
                     sum += a;
                     packed[q] |= ((uint32_t)a & 0xFFu) << (8 * r);
                 }
@@ -461,12 +461,12 @@ __global__ __launch_bounds__(256) void k_mmq_split_sum_q8(const float *__restric
         amax = fmaxf(amax, __shfl_xor(amax, 2));
         amax = fmaxf(amax, __shfl_xor(amax, 4));
         const uint16_t d16 = q8_1_scale(amax);
-        const float df = f16_bits_to_f32(d16);
+        const float df = f16_bits_to_f32(d16), rdf = q8_1_rcp(df);
         uint32_t packed = 0;
         int sum = 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int a = q8_1_code(v[t], df);
+            const int a = q8_1_code(v[t], df, rdf);
             sum += a;
             packed |= ((uint32_t)a & 0xFFu) << (8 * t);
         }

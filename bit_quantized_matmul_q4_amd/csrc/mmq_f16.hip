@@ -433,7 +433,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
                     for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
                     amax = fmaxf(amax, __shfl_xor(amax, 32));
                     const uint16_t d16 = q8_1_scale(amax);
-                    const float df = f16_bits_to_f32(d16);
+                    const float df = f16_bits_to_f32(d16), rdf = q8_1_rcp(df);
                     int sum = 0;
                     uint32_t packed[4];
 #pragma unroll
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
                         packed[q] = 0;
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const int c = q8_1_code(v[4 * q + r], df);
+                            const int c = q8_1_code(v[4 * q + r], df, rdf);
                             sum += c;
                             packed[q] |= ((uint32_t)c & 0xFFu) << (8 * r);
                         }

@@ -64,10 +64,22 @@ __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_c
 // (0 when d is 0); s16 = fp16(d * sum a), the product exact in fp32.
 __device__ __forceinline__ uint16_t q8_1_scale(float amax) { return f32_to_f16_bits(__fdiv_rn(amax, 127.0f)); }
 
-__device__ __forceinline__ int q8_1_code(float x, float df)
+// 1/d for q8_1_code: the hardware reciprocal, within one ulp.
+__device__ __forceinline__ float q8_1_rcp(float df) { return __builtin_amdgcn_rcpf(df); }
+
+// rint of the correctly rounded quotient x / d, mostly without dividing.  With
+// rdf within one ulp of 1/d, q = x * rdf is within 1.5 * 2^-23 |x / d| of the
+// exact quotient, and the rounded quotient within 2^-24 |x / d|: below 256 the
+// two lie within 2^-14 of each other, so wherever q is more than 2^-11 from a
+// half-integer both round to the same integer.  The rare quotients nearer a
+// half-integer (exact ties among them) are divided exactly.  From 256 up both
+// clamp.  d is an fp16 value, so 1/d is finite whenever d is not 0.
+__device__ __forceinline__ int q8_1_code(float x, float df, float rdf)
 {
     if (df == 0.0f) return 0;
-    const float r = rintf(__fdiv_rn(x, df));
+    const float q = x * rdf;
+    float r = rintf(q);
+    if (__builtin_expect(!(fabsf(fabsf(q - r) - 0.5f) > 0x1p-11f), 0)) r = rintf(__fdiv_rn(x, df));
     return r < -127.0f ? -127 : (r > 127.0f ? 127 : (int)r);
 }
 

@@ -66,36 +66,51 @@ __global__ __launch_bounds__(256) void k_q4_pack(const float *__restrict__ W,
     }
 }
 
-// Eight lanes per block of 32 activations, four per lane (16-byte loads).
-// The flat element index works across rows because K is a multiple of 32.
+// Eight lanes per block of 32 activations, four per lane.  A wave takes 128
+// consecutive float4 per step, two 16-byte loads per lane 1 KB apart, both in
+// flight before any arithmetic.  The flat element index works across rows
+// because K is a multiple of 32, so the eight lanes of a block are all inside
+// or all outside [0, nvec4); lanes past the end reload the last vector and
+// store nothing.  Block max and sum: DPP within each group of eight lanes.
 __global__ __launch_bounds__(256) void k_q8_1_quantize(const float *__restrict__ x,
                                                        int8_t *__restrict__ qa,
                                                        uint32_t *__restrict__ ds, int64_t nvec4)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec4; i += stride) {
-        // the 8 lanes of one block are all inside or all outside [0, nvec4)
-        const float4 v = reinterpret_cast<const float4 *>(x)[i];
-        float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
-        amax = fmaxf(amax, __shfl_xor(amax, 4));
-        const uint16_t d16 = q8_1_scale(amax);
-        const float df = f16_bits_to_f32(d16);
-        const float e[4] = {v.x, v.y, v.z, v.w};
-        uint32_t packed = 0;
-        int sum = 0;
+    constexpr int kLoads = 2;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const float4 *x4 = reinterpret_cast<const float4 *>(x);
+    for (int64_t base = wave0 * (kWave * kLoads); base < nvec4; base += nwaves * (kWave * kLoads)) {
+        float4 v[kLoads];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int a = q8_1_code(e[t], df);
-            sum += a;
-            packed |= ((uint32_t)a & 0xFFu) << (8 * t);
+        for (int h = 0; h < kLoads; ++h) v[h] = x4[min(base + kWave * h + lane, nvec4 - 1)];
+#pragma unroll
+        for (int h = 0; h < kLoads; ++h) {
+            const int64_t i = base + kWave * h + lane;
+            float amax = fmaxf(fmaxf(fabsf(v[h].x), fabsf(v[h].y)), fmaxf(fabsf(v[h].z), fabsf(v[h].w)));
+            amax = fmaxf(amax, dpp_f32<kDppQuadSwap1>(amax));
+            amax = fmaxf(amax, dpp_f32<kDppQuadSwap2>(amax));
+            amax = fmaxf(amax, dpp_f32<kDppRowHalfMirror>(amax));
+            const uint16_t d16 = q8_1_scale(amax);
+            const float df = f16_bits_to_f32(d16), rdf = q8_1_rcp(df);
+            const float e[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+            uint32_t packed = 0;
+            int sum = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int a = q8_1_code(e[t], df, rdf);
+                sum += a;
+                packed |= ((uint32_t)a & 0xFFu) << (8 * t);
+            }
+            sum += __builtin_amdgcn_update_dpp(0, sum, kDppQuadSwap1, 0xF, 0xF, false);
+            sum += __builtin_amdgcn_update_dpp(0, sum, kDppQuadSwap2, 0xF, 0xF, false);
+            sum += __builtin_amdgcn_update_dpp(0, sum, kDppRowHalfMirror, 0xF, 0xF, false);
+            if (i < nvec4) {
+                reinterpret_cast<uint32_t *>(qa)[i] = packed;
+                if ((i & 7) == 0) ds[i >> 3] = q8_1_ds(d16, df, sum);
+            }
         }
-        sum += __shfl_xor(sum, 1);
-        sum += __shfl_xor(sum, 2);
-        sum += __shfl_xor(sum, 4);
-        reinterpret_cast<uint32_t *>(qa)[i] = packed;
-        if ((i & 7) == 0) ds[i >> 3] = q8_1_ds(d16, df, sum);
     }
 }
 
@@ -119,7 +134,7 @@ hipError_t launch_q8_1_quantize(const float *x, int64_t M, int64_t K, int8_t *qa
                                 int num_cus, hipStream_t stream)
 {
     const int64_t nvec4 = M * K / 4;
-    int64_t blocks = (nvec4 + 255) / 256;
+    int64_t blocks = (nvec4 + 511) / 512;  // 512 float4 per workgroup step
     const int64_t cap = (int64_t)num_cus * 16;
     if (blocks > cap) blocks = cap;
     hipLaunchKernelGGL(k_q8_1_quantize, dim3((unsigned)blocks), dim3(256), 0, stream, x, qa,

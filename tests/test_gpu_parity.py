@@ -153,6 +153,30 @@ def test_q8_1_edge_values(q4, orc):
     assert np.array_equal(ds_g.cpu().view(torch.int16).numpy().view(np.uint16), ds_o)
 
 
+def test_q8_1_near_ties(q4, orc):
+    # quotients x / d at, and a few fp32 ulps around, half-integers, with
+    # power-of-two and general fp16 block scales from 2^-30 to 2^9 (the first
+    # value of each block, 127 d, sets d): the device takes x times a
+    # reciprocal of d and divides exactly only near half-integers
+    say("q8_1 near ties")
+    rng = np.random.default_rng(23)
+    M, K = 96, 1024
+    nb = K // 32
+    k = rng.integers(-127, 127, (M, K)).astype(np.float64)
+    e = rng.integers(-30, 10, (M, nb, 1))
+    d = np.broadcast_to(np.ldexp(1.0, e), (M, nb, 32)).reshape(M, K).copy()
+    d[M // 2:] *= 1.0 + rng.integers(1, 1024, (M - M // 2, 1)) / 1024.0
+    off = rng.choice([0.5, 0.5 + 2.0 ** -18, 0.5 - 2.0 ** -18, 0.5 + 2.0 ** -12, 0.25], (M, K))
+    x = (k + off) * d
+    x.reshape(M, nb, 32)[:, :, 0] = 127.0 * d.reshape(M, nb, 32)[:, :, 0]
+    x = x.astype(np.float32)
+    qa_o, ds_o = orc.q8_1_quantize(x)
+    qa_g, ds_g = q4.q8_1_quantize(dev(torch.from_numpy(x)))
+    torch.cuda.synchronize()
+    assert np.array_equal(qa_g.cpu().numpy(), qa_o)
+    assert np.array_equal(ds_g.cpu().view(torch.int16).numpy().view(np.uint16), ds_o)
+
+
 # ------------------------------------------------------------ block dots ---
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (32, 32, 256), (130, 200, 512), (257, 129, 768),
