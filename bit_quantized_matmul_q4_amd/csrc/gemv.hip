@@ -477,9 +477,11 @@ hipError_t dispatch_dot2(const Dot2Cfg &c, const float *x, int M, const uint8_t 
 // ------------------------------------------------------------------ arm B --
 
 // One workgroup of kBWaves waves per CU holds the activations of its K range in
-// LDS as MFMA A operands (16 activation rows x 32 k per step, fp16, zeros for
-// rows >= M), so every weight byte fetched from HBM meets its activations
-// without another global read.  Weights are the B operand (16 weight rows x 32
+// LDS as MFMA A operands (MP = 1, 2, 4, 8 or 16 activation rows x 32 k per step,
+// fp16, zeros for rows >= M; the MFMA's other rows read copies of these, so
+// the fragment reads of a small M are mostly broadcasts, and are never
+// stored), so every weight byte fetched from HBM meets its activations without
+// another global read.  Weights are the B operand (16 weight rows x 32
 // k), so the lane that loads a weight row also loads that row's scale and
 // minimum and owns the row's outputs.  GS is the (scale, minimum) group along
 // K: 256, or 32 for the group-32 format, where each MFMA step is one run of 32
@@ -487,7 +489,6 @@ hipError_t dispatch_dot2(const Dot2Cfg &c, const float *x, int M, const uint8_t 
 constexpr int kBRows = 16;                      // weight rows per unit (one MFMA column block)
 constexpr int kBWaves = 8;                      // waves per workgroup
 constexpr int kBThreads = kBWaves * kWave;
-constexpr int kBGroupLds = 8 * 4 * kBRows * 16; // A image of one group: [step 8][kg 4][m 16] x 16 B
 constexpr int kBDepth = 4;                      // (unit, group) items in flight per wave
 constexpr int kBTargetUnits = 256 * kBWaves;    // units wanted before K is split further
 constexpr int kBTileRow = 9 * 16;               // weight tile row: 8 chunks of 16 B + 16 B pad
@@ -499,13 +500,15 @@ __host__ __device__ constexpr int arm_b_fac_floats(int GS) { return GS == 32 ? 1
 __host__ __device__ constexpr int arm_b_max_groups(int GS) { return GS == 32 ? 14 : 16; }
 // per-wave tile: 16 weight rows x 144 B, and with GS 32 their 16 x 8 pairs
 __host__ __device__ constexpr int arm_b_tile_bytes(int GS) { return kBRows * kBTileRow + (GS == 32 ? kBRows * 8 * 4 : 0); }
-__host__ __device__ constexpr size_t arm_b_x_lds_bytes(int gps, int GS)
+// A image of one group with MP activation rows: [step 8][kg 4][m MP] x 16 B
+__host__ __device__ constexpr int arm_b_group_lds(int MP) { return 8 * 4 * MP * 16; }
+__host__ __device__ constexpr size_t arm_b_x_lds_bytes(int gps, int GS, int MP)
 {
-    return (size_t)gps * (kBGroupLds + 4 * arm_b_fac_floats(GS));
+    return (size_t)gps * (arm_b_group_lds(MP) + 4 * arm_b_fac_floats(GS));
 }
-__host__ __device__ constexpr size_t arm_b_lds_bytes(int gps, int GS)
+__host__ __device__ constexpr size_t arm_b_lds_bytes(int gps, int GS, int MP)
 {
-    return arm_b_x_lds_bytes(gps, GS) + (size_t)kBWaves * arm_b_tile_bytes(GS);
+    return arm_b_x_lds_bytes(gps, GS, MP) + (size_t)kBWaves * arm_b_tile_bytes(GS);
 }
 
 // Activations of groups g0 .. g0+gc-1 into LDS.  32 threads per (row m, group):
@@ -516,22 +519,54 @@ __host__ __device__ constexpr size_t arm_b_lds_bytes(int gps, int GS)
 // weights; per (group or run, row): X = sum of x and c = 7.5 * sum of (x - hi),
 // the codes' mean share of the fp16 rounding of x, folded back in exactly (the
 // remaining error is sum (x - hi) (q - 7.5), with centred codes).  Items are
-// taken kXBatch per thread at a time, all their loads issued before any is
-// used; rows >= M and items past the end read zeros (buffer bounds).
-constexpr int kXBatch = 8;
-
+// taken up to four per thread at a time, all their loads issued before any is
+// used; rows >= M and items past the end read zeros (buffer bounds), and rows
+// of items wholly past the image are skipped.  Only the MP image rows are
+// converted.  Maxima and sums over a run's 32 (or 4) lanes go by DPP within
+// rows of 16 lanes and one exchange between the two rows: the same pairs as
+// an xor butterfly, so every lane ends with the same bits.  (With five
+// shuffles per reduction this prologue took ~10 us of a 73 us call at 16
+// rows, tiny-M K 4096 N 151936; now 68.6 us in all.  All items in one round
+// trip held 110 more registers and was slower.)
+template <int NB>
 struct XGroupItems {
-    float4 a[kXBatch], b[kXBatch];
+    float4 a[NB], b[NB];
 };
+// items per thread in one round trip
+constexpr int x_batch(int MP) { return MP < 4 ? MP : 4; }
 
+__device__ __forceinline__ float run32_max(float v)
+{
+    v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
+    v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
+    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+    return fmaxf(v, __shfl_xor(v, 16));
+}
+
+template <int L>
+__device__ __forceinline__ float run_sum(float v)
+{
+    static_assert(L == 4 || L == 32, "runs of 4 or 32 lanes");
+    v += dpp_f32<kDppQuadSwap1>(v);
+    v += dpp_f32<kDppQuadSwap2>(v);
+    if (L == 32) {
+        v += dpp_f32<kDppRowHalfMirror>(v);
+        v += dpp_f32<kDppRowMirror>(v);
+        v += __shfl_xor(v, 16);
+    }
+    return v;
+}
+
+template <int MP>
 __device__ __forceinline__ void load_x_groups(rsrc_t rx, int M, int K, int g0, int gc, int base,
-                                              XGroupItems &v)
+                                              XGroupItems<x_batch(MP)> &v)
 {
 #pragma unroll
-    for (int it = 0; it < kXBatch; ++it) {
+    for (int it = 0; it < x_batch(MP); ++it) {
         const int idx = base + threadIdx.x + it * kBThreads;
         const int pair = idx >> 5, sub = idx & 31;
-        const int m = pair & (kBRows - 1), gl = pair >> 4;
+        const int m = pair & (MP - 1), gl = pair / MP;
         const int c = sub >> 2, t = sub & 3;
         const bool ok = m < M && gl < gc;
         const uint32_t off =
@@ -541,30 +576,32 @@ __device__ __forceinline__ void load_x_groups(rsrc_t rx, int M, int K, int g0, i
     }
 }
 
-template <int GS>
-__device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupItems &v, uint8_t *lds)
+template <int GS, int MP>
+__device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupItems<x_batch(MP)> &v, uint8_t *lds)
 {
-    float *fac = reinterpret_cast<float *>(lds + (size_t)gc * kBGroupLds);
+    float *fac = reinterpret_cast<float *>(lds + (size_t)gc * arm_b_group_lds(MP));
     constexpr int F = arm_b_fac_floats(GS);
+    const int nx = MP * gc * 32;
 #pragma unroll
-    for (int it = 0; it < kXBatch; ++it) {
+    for (int it = 0; it < x_batch(MP); ++it) {
+        // rows of items wholly past the image (few groups per K split): skipped
+        // by the whole workgroup
+        if (base + it * kBThreads >= nx) break;
         const int idx = base + threadIdx.x + it * kBThreads;
         const int pair = idx >> 5, sub = idx & 31;
-        const int m = pair & (kBRows - 1), gl = pair >> 4;
+        const int m = pair & (MP - 1), gl = pair / MP;
         const int c = sub >> 2, t = sub & 3;
         const float4 a = v.a[it], b = v.b[it];
         float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
                            fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
         // the power-of-two scale is per group of 256; the sums per (scale, minimum) group
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        amax = run32_max(amax);
         const int sc = chunk_exp(amax);
         const float ls = ldexpf(1.0f, -sc), hs = ldexpf(1.0f, -sc - 4);
         // sum of x on the scaled values (as in arm A)
         float sum = ((a.x * ls + a.y * ls) + (a.z * ls + a.w * ls)) +
                     ((b.x * ls + b.y * ls) + (b.z * ls + b.w * ls));
-#pragma unroll
-        for (int o = 1; o < GS / 8; o <<= 1) sum += __shfl_xor(sum, o);
+        sum = run_sum<GS / 8>(sum);
         sum = ldexpf(sum, sc - kYShift);
         // slot order of one widened dword: (4t, 4t+2) (16+4t, 16+4t+2) (4t+1, 4t+3) (16+4t+1, 16+4t+3)
         const float w[8] = {a.x * ls, a.z * ls, b.x * hs, b.z * hs, a.y * ls, a.w * ls, b.y * hs, b.w * hs};
@@ -578,13 +615,12 @@ __device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupI
             hw[p] = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
         }
         float delta = ldexpf(dl, sc - kYShift) + ldexpf(dh, sc + 4 - kYShift);
-#pragma unroll
-        for (int o = 1; o < GS / 8; o <<= 1) delta += __shfl_xor(delta, o);
+        delta = run_sum<GS / 8>(delta);
         if (gl < gc) {
             // GS 256: step d mixes runs (kg = run & 3, d = (run >> 2) * 4 + dword);
             // GS 32: step d is run d, lane kg its dword kg
             const int kg = GS == 32 ? t : (c & 3), d = GS == 32 ? c : (c >> 2) * 4 + t;
-            *reinterpret_cast<uint4 *>(lds + (size_t)gl * kBGroupLds + ((d * 4 + kg) * kBRows + m) * 16) =
+            *reinterpret_cast<uint4 *>(lds + (size_t)gl * arm_b_group_lds(MP) + ((d * 4 + kg) * MP + m) * 16) =
                 make_uint4(hw[0], hw[1], hw[2], hw[3]);
             float *fg = fac + gl * F;
             if (sub == 0) fg[m] = ldexpf(1.0f, 24 - kYShift + sc);
@@ -615,7 +651,7 @@ __device__ __forceinline__ void convert_x_groups(int gc, int base, const XGroupI
 // GS 32: step d is run d (lane (j, kg) its dword kg); the lane that loads a
 // run also loads the run's pair, which goes through the tile with the codes.
 // Items past the wave's end load out of range (zeros) and write nothing.
-template <int D, bool kSmQuad, int GS>
+template <int D, bool kSmQuad, int GS, int MP>
 __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict__ x,
                                                          const uint8_t *__restrict__ qs,
                                                          const uint32_t *__restrict__ sm,
@@ -640,7 +676,7 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
     const uint32_t rowbytes = K / 2;
     // partials [split][M][ldo] (or y itself): the host keeps every offset below 2^31
     const rsrc_t r_out = make_rsrc(out + (int64_t)split * M * ldo, (uint32_t)(((int64_t)(M - 1) * ldo + N) * 4));
-    uint8_t *tile = xl + arm_b_x_lds_bytes(gc, GS) + wave * arm_b_tile_bytes(GS);
+    uint8_t *tile = xl + arm_b_x_lds_bytes(gc, GS, MP) + wave * arm_b_tile_bytes(GS);
     uint32_t *tile_sm = reinterpret_cast<uint32_t *>(tile + kBRows * kBTileRow);  // GS 32: [row][run]
 
     const rsrc_t r_qs = make_rsrc(qs, (uint32_t)N * rowbytes);
@@ -675,9 +711,9 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
     };
     // activation loads first, then the weight ring, then the conversion
     const rsrc_t r_x = make_rsrc(x, (uint32_t)M * K * 4u);
-    const int nx = kBRows * gc * 32;
-    XGroupItems xv;
-    load_x_groups(r_x, M, K, g0, gc, 0, xv);
+    const int nx = MP * gc * 32;
+    XGroupItems<x_batch(MP)> xv;
+    load_x_groups<MP>(r_x, M, K, g0, gc, 0, xv);
     int lu = 0, lg = 0;  // next item to load
 #pragma unroll
     for (int s = 0; s < D; ++s) {
@@ -685,14 +721,14 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
         if (kSmQuad && s % 4 == 3) load_quad(s / 4, lu, lg - 3);
         if (++lg == gc) { lg = 0; ++lu; }
     }
-    convert_x_groups<GS>(gc, 0, xv, xl);
-    for (int base = kXBatch * kBThreads; base < nx; base += kXBatch * kBThreads) {
-        load_x_groups(r_x, M, K, g0, gc, base, xv);
-        convert_x_groups<GS>(gc, base, xv, xl);
+    convert_x_groups<GS, MP>(gc, 0, xv, xl);
+    for (int base = x_batch(MP) * kBThreads; base < nx; base += x_batch(MP) * kBThreads) {
+        load_x_groups<MP>(r_x, M, K, g0, gc, base, xv);
+        convert_x_groups<GS, MP>(gc, base, xv, xl);
     }
     __syncthreads();
 
-    const float *fac = reinterpret_cast<const float *>(xl + (size_t)gc * kBGroupLds);
+    const float *fac = reinterpret_cast<const float *>(xl + (size_t)gc * arm_b_group_lds(MP));
     float4_t yacc = {0.f, 0.f, 0.f, 0.f};
     int cu = 0, cg = 0;  // item being computed
     for (int base = 0; base < nitems; base += D) {
@@ -725,16 +761,20 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
             if (kSmQuad && s % 4 == 3) load_quad(s / 4, lu, lg - 3);
             if (++lg == gc) { lg = 0; ++lu; }
 
-            const uint8_t *ag = xl + (size_t)cg * kBGroupLds + (kg * kBRows + j) * 16;
+            // lane (j, kg) reads image row j mod MP; its factors those of rows
+            // 4 kg' .. 4 kg' + 3, kg' = kg mod MP/4 (0 below four rows; rows
+            // past MP are copies or unset, and never stored)
+            const int kq = MP >= 4 ? (kg & (MP / 4 - 1)) : 0;
+            const uint8_t *ag = xl + (size_t)cg * arm_b_group_lds(MP) + (kg * MP + (j & (MP - 1))) * 16;
             const float *fg = fac + cg * F;
-            const float4 f = *reinterpret_cast<const float4 *>(fg + 4 * kg);
+            const float4 f = *reinterpret_cast<const float4 *>(fg + 4 * kq);
             if (kG32) {
                 // one MFMA per run, each with its own (scale, minimum); two
                 // accumulators so a run's epilogue overlaps the next product
                 float4_t accs[2];
 #pragma unroll
                 for (int d = 0; d < 8; ++d) {
-                    const half8_t a = *reinterpret_cast<const half8_t *>(ag + d * 4 * kBRows * 16);
+                    const half8_t a = *reinterpret_cast<const half8_t *>(ag + d * 4 * MP * 16);
                     const uint4 c4 = d < 4 ? bw0 : bw1;
                     const uint32_t w = (d & 3) == 0 ? c4.x : (d & 3) == 1 ? c4.y : (d & 3) == 2 ? c4.z : c4.w;
                     uint32_t p[4];
@@ -746,8 +786,8 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
                         const float4_t acc = accs[dp & 1];
                         const uint32_t sv = tile_sm[j * 8 + dp];
                         const float sf = f16_bits_to_f32(sv & 0xFFFFu), mf = f16_bits_to_f32(sv >> 16);
-                        const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + dp * kBRows + 4 * kg);
-                        const float4 cc = *reinterpret_cast<const float4 *>(fg + 9 * kBRows + dp * kBRows + 4 * kg);
+                        const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + dp * kBRows + 4 * kq);
+                        const float4 cc = *reinterpret_cast<const float4 *>(fg + 9 * kBRows + dp * kBRows + 4 * kq);
                         yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
                         yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
                         yacc[2] = fmaf(sf, fmaf(f.z, acc[2], cc.z), fmaf(mf, X.z, yacc[2]));
@@ -758,8 +798,8 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
                     const float4_t acc = accs[1];
                     const uint32_t sv = tile_sm[j * 8 + 7];
                     const float sf = f16_bits_to_f32(sv & 0xFFFFu), mf = f16_bits_to_f32(sv >> 16);
-                    const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + 7 * kBRows + 4 * kg);
-                    const float4 cc = *reinterpret_cast<const float4 *>(fg + 9 * kBRows + 7 * kBRows + 4 * kg);
+                    const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + 7 * kBRows + 4 * kq);
+                    const float4 cc = *reinterpret_cast<const float4 *>(fg + 9 * kBRows + 7 * kBRows + 4 * kq);
                     yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
                     yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
                     yacc[2] = fmaf(sf, fmaf(f.z, acc[2], cc.z), fmaf(mf, X.z, yacc[2]));
@@ -770,7 +810,7 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
                 float4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
                 for (int d = 0; d < 8; ++d) {
-                    const half8_t a = *reinterpret_cast<const half8_t *>(ag + d * 4 * kBRows * 16);
+                    const half8_t a = *reinterpret_cast<const half8_t *>(ag + d * 4 * MP * 16);
                     const uint4 c4 = d < 4 ? bw0 : bw1;
                     const uint32_t w = (d & 3) == 0 ? c4.x : (d & 3) == 1 ? c4.y : (d & 3) == 2 ? c4.z : c4.w;
                     uint32_t p[4];
@@ -779,8 +819,8 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
                     acc2[d & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc2[d & 1], 0, 0, 0);
                 }
                 const float4_t acc = acc2[0] + acc2[1];
-                const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + 4 * kg);
-                const float4 cc = *reinterpret_cast<const float4 *>(fg + 2 * kBRows + 4 * kg);
+                const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + 4 * kq);
+                const float4 cc = *reinterpret_cast<const float4 *>(fg + 2 * kBRows + 4 * kq);
                 const float sf = f16_bits_to_f32(smv & 0xFFFFu), mf = f16_bits_to_f32(smv >> 16);
                 yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
                 yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
@@ -841,12 +881,18 @@ MfmaCfg choose_mfma(int64_t N, int K, int GS)
     return c;
 }
 
-template <int GS>
-hipError_t launch_arm_b(const MfmaCfg &c, const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
-                        int64_t ldy, int K, float *y, void *workspace, size_t ws_bytes, const DeviceInfo &dev,
-                        hipStream_t stream)
+// Activation rows of the image for an M-row call.  With fewer rows than the
+// MFMA's 16 the fragment reads repeat rows: tiny-M K 4096 N 151936 at M = 4
+// 72.3 -> 60.6 us, M = 8 70.4 -> 63.0 us, bit-identical (12 or 16 waves per
+// workgroup, in the LDS this frees, were slower).
+constexpr int arm_b_image_rows(int M) { return M <= 2 ? M : (M <= 4 ? 4 : (M <= 8 ? 8 : 16)); }
+
+template <int GS, int MP>
+hipError_t launch_arm_b_mp(const MfmaCfg &c, const float *x, int M, const uint8_t *qs, const uint16_t *sm,
+                           int64_t N, int64_t ldy, int K, float *y, void *workspace, size_t ws_bytes,
+                           const DeviceInfo &dev, hipStream_t stream)
 {
-    const size_t lds = arm_b_lds_bytes(c.gps, GS);
+    const size_t lds = arm_b_lds_bytes(c.gps, GS, MP);
     if (lds > (size_t)dev.lds_bytes) return hipErrorInvalidConfiguration;
     const int64_t R = (N + kBRows - 1) / kBRows;
     // workgroups per split: one per CU overall, at most one per kBWaves units
@@ -865,16 +911,18 @@ hipError_t launch_arm_b(const MfmaCfg &c, const float *x, int M, const uint8_t *
     // offsets (the C ABI rejects shapes beyond it, so this does not trigger)
     if (((int64_t)(M - 1) * ldo + N) * 4 > kMaxBufferBytes) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(wps * c.nsplit)), block(kBThreads);
-    if (GS == 32) {
-        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, false, 32>), grid, block, lds, stream, x, qs, sm32, out, ldo,
-                           M, (int)N, K, c.gps, c.nsplit, (int)wps);
-    } else if ((K / kGroup) % c.gps == 0 && c.gps % 4 == 0) {
-        // (scale, minimum) quads need every split's group count to be a multiple of 4
-        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, true, kGroup>), grid, block, lds, stream, x, qs, sm32, out,
+    if constexpr (GS == 32) {
+        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, false, 32, MP>), grid, block, lds, stream, x, qs, sm32, out,
                            ldo, M, (int)N, K, c.gps, c.nsplit, (int)wps);
     } else {
-        hipLaunchKernelGGL((k_gemv_mfma<kBDepth, false, kGroup>), grid, block, lds, stream, x, qs, sm32, out,
-                           ldo, M, (int)N, K, c.gps, c.nsplit, (int)wps);
+        if ((K / kGroup) % c.gps == 0 && c.gps % 4 == 0) {
+            // (scale, minimum) quads need every split's group count to be a multiple of 4
+            hipLaunchKernelGGL((k_gemv_mfma<kBDepth, true, kGroup, MP>), grid, block, lds, stream, x, qs, sm32,
+                               out, ldo, M, (int)N, K, c.gps, c.nsplit, (int)wps);
+        } else {
+            hipLaunchKernelGGL((k_gemv_mfma<kBDepth, false, kGroup, MP>), grid, block, lds, stream, x, qs,
+                               sm32, out, ldo, M, (int)N, K, c.gps, c.nsplit, (int)wps);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.nsplit == 1) return e;
@@ -884,6 +932,20 @@ hipError_t launch_arm_b(const MfmaCfg &c, const float *x, int M, const uint8_t *
     hipLaunchKernelGGL(k_splitk_sum, dim3((unsigned)sb), dim3(256), 0, stream, out, y, M, (int)N, ldy,
                        c.nsplit);
     return hipGetLastError();
+}
+
+template <int GS>
+hipError_t launch_arm_b(const MfmaCfg &c, const float *x, int M, const uint8_t *qs, const uint16_t *sm, int64_t N,
+                        int64_t ldy, int K, float *y, void *workspace, size_t ws_bytes, const DeviceInfo &dev,
+                        hipStream_t stream)
+{
+    switch (arm_b_image_rows(M)) {
+    case 1: return launch_arm_b_mp<GS, 1>(c, x, M, qs, sm, N, ldy, K, y, workspace, ws_bytes, dev, stream);
+    case 2: return launch_arm_b_mp<GS, 2>(c, x, M, qs, sm, N, ldy, K, y, workspace, ws_bytes, dev, stream);
+    case 4: return launch_arm_b_mp<GS, 4>(c, x, M, qs, sm, N, ldy, K, y, workspace, ws_bytes, dev, stream);
+    case 8: return launch_arm_b_mp<GS, 8>(c, x, M, qs, sm, N, ldy, K, y, workspace, ws_bytes, dev, stream);
+    default: return launch_arm_b_mp<GS, 16>(c, x, M, qs, sm, N, ldy, K, y, workspace, ws_bytes, dev, stream);
+    }
 }
 
 }  // namespace
@@ -897,16 +959,20 @@ constexpr int kArmAMaxK2 = 31744;
 constexpr int kArmAMaxK4 = 15360;
 
 // Activation rows arm A's image holds for an M-row call (0: the matrix-core
-// arm).  One and two rows always (measured faster at every N); three and four
-// rows only below 65536 weight rows: there the matrix-core arm's fixed costs
+// arm).  One row always (measured faster at every N).  Three and four rows
+// only below 65536 weight rows: there the matrix-core arm's fixed costs
 // (activation image per workgroup, K split with a second pass) dominate
 // (4096 x 4096 at M = 4: 9.8 vs 20.6 us), while on the lm_head widths four
-// rows make arm A VALU-bound (88 vs 72 us at K = 4096).
+// rows make arm A VALU-bound (88 vs 72 us at K = 4096).  Two rows likewise,
+// except that from 65536 weight rows the matrix-core arm's two-row image wins
+// only where it takes K without a split (K <= 4096: tiny-M K 4096 N 151936
+// 62.9 -> 56.9 us, K 2560 42.1 -> 39.3 us; K 12288 N 65536, three splits,
+// 82.0 vs 86.5 us).
 constexpr int64_t kArmA4MaxN = 65536;
 int arm_a_rows(int64_t M, int64_t N, int64_t K)
 {
     if (M == 1 && K <= kArmAMaxK) return 1;
-    if (M == 2 && K <= kArmAMaxK2) return 2;
+    if (M == 2 && K <= kArmAMaxK2 && (N < kArmA4MaxN || K > 16 * kGroup)) return 2;
     if (M >= 3 && M <= 4 && K <= kArmAMaxK4 && N < kArmA4MaxN) return 4;
     return 0;
 }

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void k_q4_pack(const float *__restrict__ W,
 
 // Eight lanes per block of 32 activations, four per lane.  A wave takes 128
 // consecutive float4 per step, two 16-byte loads per lane 1 KB apart, both in
-// flight before any arithmetic.  The flat element index works across rows
+// flight before any arithmetic (non-temporal: x is read once).  The flat element index works across rows
 // because K is a multiple of 32, so the eight lanes of a block are all inside
 // or all outside [0, nvec4); lanes past the end reload the last vector and
 // store nothing.  Block max and sum: DPP within each group of eight lanes.
@@ -84,7 +84,9 @@ __global__ __launch_bounds__(256) void k_q8_1_quantize(const float *__restrict__
     for (int64_t base = wave0 * (kWave * kLoads); base < nvec4; base += nwaves * (kWave * kLoads)) {
         float4 v[kLoads];
 #pragma unroll
-        for (int h = 0; h < kLoads; ++h) v[h] = x4[min(base + kWave * h + lane, nvec4 - 1)];
+        for (int h = 0; h < kLoads; ++h)
+            v[h] = __builtin_bit_cast(float4, __builtin_nontemporal_load(reinterpret_cast<const float4_t *>(x4) +
+                                                                         min(base + kWave * h + lane, nvec4 - 1)));
 #pragma unroll
         for (int h = 0; h < kLoads; ++h) {
             const int64_t i = base + kWave * h + lane;

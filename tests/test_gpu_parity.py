@@ -280,10 +280,12 @@ def test_gemv_rows_match_single_row_calls(q4, orc):
 
 
 # (M, N, K, seed, VALU arm): up to 4 rows run the one-row arm when the image
-# fits (K <= 31744 for 2 rows, 15360 for 4) and, for 3-4 rows, N < 65536
+# fits (K <= 31744 for 2 rows, 15360 for 4) and, for 3-4 rows, N < 65536; for
+# 2 rows, N < 65536 or K > 4096
 FEW_ROW_CASES = [(2, 700, 2560, 21, True), (2, 37984, 4096, 22, True), (2, 300, 31744, 23, True),
                  (2, 96, 32000, 24, False), (3, 700, 2560, 25, True), (4, 1000, 15360, 26, True),
-                 (4, 300, 15616, 27, False), (4, 65535, 2560, 28, True), (4, 65536, 2560, 29, False)]
+                 (4, 300, 15616, 27, False), (4, 65535, 2560, 28, True), (4, 65536, 2560, 29, False),
+                 (2, 65535, 4096, 30, True), (2, 65536, 4096, 31, False), (2, 65536, 4352, 32, True)]
 
 
 @pytest.mark.parametrize("M,N,K,seed,valu", FEW_ROW_CASES)
@@ -437,11 +439,12 @@ def test_mmq_split_k_pp256_down(q4, orc):
 
 
 def test_gemv_k_beyond_one_workgroup(q4, orc):
-    # K = 65792: the M = 1 activation image no longer fits one workgroup's
-    # LDS, so M = 1 runs on the matrix-core arm with K split over workgroups
+    # K = 65792: the M = 1 and M = 2 activation images no longer fit one
+    # workgroup's LDS, so they run on the matrix-core arm (one- and two-row
+    # images) with K split over workgroups
     K = 65792
     assert q4.q4_gemv_workspace_bytes(1, 100, K) > 0
-    for M in (1, 3):
+    for M in (1, 2, 3):
         say("gemv M=%d N=100 K=%d" % (M, K))
         W, x = wl.gemv_case(50 + M, M, 100, K)
         qs, sm = q4.q4_pack(dev(W))
