@@ -62,7 +62,13 @@ constexpr int kFn = 128;           // weight rows per tile
 constexpr int kFk = 64;            // K per step: two Q8_1 blocks
 constexpr int kFThreads = 256;
 constexpr int kStepVecs = 8 * kFm; // 16-byte vectors of the image per (tile, step)
-constexpr int kGemmThreads = 512;
+// Computing waves (one per SIMD) and the 32-row activation tiles each owns.
+// Eight computing waves (two per SIMD, 64 x 64 each, 129 registers) were
+// 3-6 % slower at M 512-2048: each weight tile's fragments are then read and
+// unpacked by four waves instead of two.
+constexpr int kCW = 4;
+constexpr int kTI = kFm / 32 / (kCW / 2);
+constexpr int kGemmThreads = (kCW + 4) * kWave;  // and one loading wave per SIMD
 constexpr int kStages = 4;                      // K steps in LDS at once
 constexpr int kStageVecs = kStepVecs + 2 * kFn; // image + packed weights of a step
 constexpr int kSmVecs32 = 2 * kFn / 4;          // group 32: the step's (scale, minimum) pairs
@@ -251,8 +257,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool consumer = wave < 4;
-    const int wn = wave & 1, wm = (wave >> 1) & 1, pw = wave - 4;
+    const bool consumer = wave < kCW;
+    const int wn = wave & 1, wm = (wave >> 1) & (kCW / 2 - 1), pw = wave - kCW;
     const int l32 = lane & 31, h = lane >> 5;
     const int S = K / kFk, G = K / kGroup;
     const int P = kG32 ? K / kBlock : G;
@@ -339,20 +345,20 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     }
 
     // ---- consumer ----
-    float16_t acc[2][4];
+    float16_t acc[2][kTI];
     auto zero_acc = [&]() {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kTI; ++i)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
     };
     zero_acc();
-    auto read_frags = [&](int u, int t, f16x8 (&bv)[4]) {
-        const int4_t *act = lds + (u % kStages) * kSV + wm * 128 + l32;
+    auto read_frags = [&](int u, int t, f16x8 (&bv)[kTI]) {
+        const int4_t *act = lds + (u % kStages) * kSV + wm * (32 * kTI) + l32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bv[i] = __builtin_bit_cast(f16x8, act[(2 * t + h) * kFm + 32 * i]);
+        for (int i = 0; i < kTI; ++i) bv[i] = __builtin_bit_cast(f16x8, act[(2 * t + h) * kFm + 32 * i]);
     };
     auto read_wts = [&](int u, int4_t (&wq)[2]) {
         const int4_t *wv = lds + (u % kStages) * kSV + kStepVecs + h * kFn + wn * 64 + l32;
@@ -388,21 +394,21 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
             av[j] = f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
         }
     };
-    auto mfmas = [&](const f16x8 (&av)[2], const f16x8 (&bv)[4]) {
+    auto mfmas = [&](const f16x8 (&av)[2], const f16x8 (&bv)[kTI]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kTI; ++i)
                 acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[j], bv[i], acc[j][i], 0, 0, 0);
     };
     // the row factors of tile k's activation rows, loaded when the tile
     // starts and used by its epilogue
-    float fin[4];
+    float fin[kTI];
     auto load_factors = [&](int k) {
         const int m0 = (tile_of(k) % tiles_m) * kFm;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + wm * 128 + 32 * i + l32;
+        for (int i = 0; i < kTI; ++i) {
+            const int m = m0 + wm * (32 * kTI) + 32 * i + l32;
             fin[i] = m < M ? fs[m] : 1.0f;
         }
     };
@@ -415,8 +421,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
         for (int j = 0; j < 2; ++j) {
             const int nl = wn * 64 + 32 * j;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * 128 + 32 * i + l32;
+            for (int i = 0; i < kTI; ++i) {
+                const int m = m0 + wm * (32 * kTI) + 32 * i + l32;
                 const float fi = m < M ? 1.0f / fin[i] : 0.0f;
                 const float16_t &a = acc[j][i];
                 float v[16];
@@ -481,7 +487,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     // last).
     auto interleave = [&]() {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 2 * kTI; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     };
     load_factors(0);
     wait_vm_barrier<63>();  // B_init (consumers wait for no loads of their own)
-    f16x8 bv0[4], bv1[4], av0[2], av1[2];
+    f16x8 bv0[kTI], bv1[kTI], av0[2], av1[2];
     int4_t wq[2];
     read_wts(0, wq);
     consts(0);
