@@ -246,6 +246,15 @@ def test_gemv_parity_small(q4, orc, M, N, K):
     gemv_case_check(q4, orc, M, N, K, N + K, "gemv %dx%dx%d" % (M, N, K))
 
 
+# matrix-core arm with activation images of 4, 8 and 16 rows holding fewer
+# rows than that (zero rows between M and the image, copies past it)
+@pytest.mark.parametrize("M,N,K", [(3, 65536, 512), (6, 700, 2560), (7, 1000, 4096), (9, 300, 2560),
+                                   (12, 513, 1280), (15, 700, 9216)])
+def test_gemv_matrix_core_partial_images(q4, orc, M, N, K):
+    say("gemv matrix-core arm M=%d N=%d K=%d" % (M, N, K))
+    gemv_case_check(q4, orc, M, N, K, 7 * M + N, "gemv %dx%dx%d" % (M, N, K))
+
+
 def test_gemv_single_4096(q4, orc):
     c = wl.SINGLE_GEMV
     say("gemv single 4096x4096 seed 0")
