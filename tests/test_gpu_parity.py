@@ -582,6 +582,31 @@ def f16_workspace(M, N, K):
     return rows * K * 2 + rows * 4 + (N + 127) // 128 * 128 * 8
 
 
+@pytest.mark.parametrize("design,M,N,K", [("f16", 1024, 8192, 512), ("int8", 300, 200, 768),
+                                          ("int8", 2048, 256, 4096)])
+def test_mmq_layout_probe(q4, orc, design, M, N, K):
+    # one nonzero activation per row, at k = m mod K: y[m][n] is that value
+    # (as Q8_1 holds it) times the dequantized W[n][m mod K], so every
+    # (m, n, k) place of the operand layouts meets its own weight; the
+    # expectation uses the oracle's dequantizers only, not its product
+    say("mmq layout probe (%s design) M=%d N=%d K=%d" % (design, M, N, K))
+    if design == "f16":
+        assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, N, K)
+    W, _ = wl.gemv_case(M + N, 1, N, K)
+    rows, ks = np.arange(M), np.arange(M) % K
+    x = np.zeros((M, K), dtype=np.float32)
+    x[rows, ks] = 1.0 + (rows % 7) / 8.0
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(torch.from_numpy(x)))
+    gemm = q4.q4_mmq_gemm if design == "f16" else q4.q4_mmq_gemm_int8
+    y = gemm(qa, ds, qs, sm).cpu().numpy()
+    wdq = orc.q4_dequant(qs.cpu().numpy(), sm.cpu().view(torch.int16).numpy().view(np.uint16), K)
+    xdq = orc.q8_1_dequant(qa.cpu().numpy(), ds.cpu().view(torch.int16).numpy().view(np.uint16))
+    ref = xdq[rows, ks][:, None] * wdq[:, ks].T
+    assert np.count_nonzero(xdq) == M
+    close(y, ref, "mmq layout probe " + design)
+
+
 def test_mmq_f16_ragged(q4, orc):
     # 2 x 100 tiles, both edges ragged (300 = 256 + 44 rows, 12700 = 99 * 128 + 28)
     M, N, K = 300, 12700, 512
