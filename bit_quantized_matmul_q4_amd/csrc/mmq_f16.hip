@@ -478,13 +478,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
         }
     };
 
-    // Each round's fragments and weights are read and unpacked during the
-    // round before: one scheduling region holds a round's 8 MFMAs and the
-    // next round's LDS reads and unpack, interleaved one MFMA, one read and
-    // three VALU ops at a time so the VALU runs in the MFMAs' shadow.  B_u
-    // falls between rounds 2 and 3, and step u + 1's first operands are read
-    // after it, during round 3 (the next tile's first step after a tile's
-    // last).
+    // Each round's activation fragments are read two rounds ahead (four
+    // fragment buffers; one round ahead, the loading waves' LDS writes left
+    // the reads late: M 2048 4096 -> 12288 261 -> 254 us, 12288 -> 4096 257
+    // -> 246 us, bit-identical) and its weights unpacked during the round
+    // before: one scheduling region holds a round's 8 MFMAs, LDS reads and
+    // unpack, interleaved one MFMA, one read and three VALU ops at a time so
+    // the VALU runs in the MFMAs' shadow.  B_u falls between rounds 1 and 2,
+    // and step u + 1's first fragments are read after it, during rounds 2 and
+    // 3 (the next tile's first step after a tile's last); the group
+    // constants of step u + 1 change only after round 2 has unpacked step u's
+    // last weights.
     auto interleave = [&]() {
 #pragma unroll
         for (int k = 0; k < 2 * kTI; ++k) {
@@ -495,36 +499,37 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     };
     load_factors(0);
     wait_vm_barrier<63>();  // B_init (consumers wait for no loads of their own)
-    f16x8 bv0[kTI], bv1[kTI], av0[2], av1[2];
+    f16x8 bv0[kTI], bv1[kTI], bv2[kTI], bv3[kTI], av0[2], av1[2];
     int4_t wq[2];
     read_wts(0, wq);
     consts(0);
     read_frags(0, 0, bv0);
+    read_frags(0, 1, bv1);
     unpack(0, wq, av0);
 #pragma unroll 1
     for (int u = 0; u < U; ++u) {
         __builtin_amdgcn_sched_barrier(0);
         mfmas(av0, bv0);                       // round 0
-        read_frags(u, 1, bv1);
+        read_frags(u, 2, bv2);
         unpack(1, wq, av1);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
         mfmas(av1, bv1);                       // round 1
-        read_frags(u, 2, bv0);
+        read_frags(u, 3, bv3);
         unpack(2, wq, av0);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(av0, bv0);                       // round 2
-        read_frags(u, 3, bv1);
-        unpack(3, wq, av1);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
         wait_vm_barrier<63>();                 // B_u: step u + 1 in LDS
         int4_t wqn[2];
         read_wts(u + 1, wqn);
-        if (kG32 || ((u + 1) & 3) == 0) consts(u + 1);
-        mfmas(av1, bv1);                       // round 3
+        mfmas(av0, bv2);                       // round 2
         read_frags(u + 1, 0, bv0);
+        unpack(3, wq, av1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kG32 || ((u + 1) & 3) == 0) consts(u + 1);
+        mfmas(av1, bv3);                       // round 3
+        read_frags(u + 1, 1, bv1);
         unpack(0, wqn, av0);
         interleave();
         wq[0] = wqn[0];
