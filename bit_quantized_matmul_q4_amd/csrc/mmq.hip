@@ -616,6 +616,26 @@ bool mmq_int8_pipelined(int64_t M, int64_t N, int64_t K)
     return tiles >= 128 && mmqi_supported(M, N, K);
 }
 
+// fp32 and Q8_1 output (group-32 weights have no pipelined integer kernel):
+// where the pipelined kernel's 128 x 128 tiles fill the CUs in one round (at
+// most 256) it beats the fp16 design, whose 256 x 128 tiles then leave at
+// least half the CUs idle (measured, q4_mmq_gemm_int8 vs the fp16 route, us:
+// 1024 x 12288 -> 4096 152 vs 188; 512 x 4096 -> 8192 57 vs 72; 2048 x 4096
+// -> 2048 56 vs 74; 256 x 4096 -> 16384 56 vs 69; 640 x 4096 -> 6144, 240
+// tiles, 53 vs 70; with 288 tiles, 512 x 2560 -> 9216, the fp16 design stays
+// faster, 53 vs 65).
+bool mmq_int8_one_round(int64_t M, int64_t N, int64_t K)
+{
+    constexpr int64_t kCus = 256;
+    return mmq_int8_pipelined(M, N, K) && ((M + 127) / 128) * ((N + 127) / 128) <= kCus;
+}
+
+// the fp32- and Q8_1-output routes' choice
+bool mmq_f32_uses_f16(int64_t M, int64_t N, int64_t K)
+{
+    return mmq_uses_f16(M, N, K) && !mmq_int8_one_round(M, N, K);
+}
+
 size_t mmq_int8_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < kGroup) return 0;
@@ -633,9 +653,10 @@ size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < kGroup) return 0;
     // the K-split partials of k_mmq (Q8_1 output and group-32 weights take it
-    // at any grid), what k_mmqi needs where the call routes to it, the fp16
-    // design's image
-    size_t need = mmq_uses_f16(M, N, K) ? 0 : mmq_int8_workspace_bytes(M, N, K);
+    // at any grid the other designs do not), what k_mmqi needs where the fp32
+    // and Q8_1 routes take it, the fp16 design's image (the group-32 route
+    // takes it wherever mmq_uses_f16 holds)
+    size_t need = mmq_f32_uses_f16(M, N, K) ? 0 : mmq_int8_workspace_bytes(M, N, K);
     {
         const SplitCfg sc = choose_split(M, N, (int)K);
         if (sc.nsplit > 1) {
@@ -657,7 +678,8 @@ hipError_t launch_mmq_int8(const int8_t *qa, const uint16_t *ds, int64_t M, cons
                            const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
                            const DeviceInfo &dev, hipStream_t stream)
 {
-    if (mmq_int8_pipelined(M, N, K)) return launch_mmqi(qa, ds, M, qs, sm, N, K, y, workspace, stream);
+    if (mmq_int8_pipelined(M, N, K))
+        return launch_mmqi(qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, workspace, stream);
     return run_tiles(kOutY, false, qa, ds, M, qs, sm, N, K, y, nullptr, nullptr, nullptr, workspace,
                      dev.num_cus, stream);
 }
@@ -666,7 +688,7 @@ hipError_t launch_mmq(const int8_t *qa, const uint16_t *ds, int64_t M, const uin
                       const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
                       const DeviceInfo &dev, hipStream_t stream)
 {
-    if (mmq_uses_f16(M, N, K))
+    if (mmq_f32_uses_f16(M, N, K))
         return launch_mmqf(qa, ds, M, qs, sm, N, K, false, y, nullptr, nullptr, workspace, dev.num_cus, stream);
     return launch_mmq_int8(qa, ds, M, qs, sm, N, K, y, workspace, dev, stream);
 }
@@ -685,7 +707,11 @@ hipError_t launch_mmq_q8_1(const int8_t *qa, const uint16_t *ds, int64_t M, cons
                            const uint16_t *sm, int64_t N, int K, int8_t *qo, uint16_t *dso,
                            void *workspace, const DeviceInfo &dev, hipStream_t stream)
 {
-    if (mmq_uses_f16(M, N, K))
+    // the design the fp32 route takes for the shape, so the result is that
+    // route's fp32 output quantized
+    if (!mmq_f32_uses_f16(M, N, K) && mmq_int8_pipelined(M, N, K))
+        return launch_mmqi(qa, ds, M, qs, sm, N, K, nullptr, qo, dso, workspace, stream);
+    if (mmq_f32_uses_f16(M, N, K))
         return launch_mmqf(qa, ds, M, qs, sm, N, K, false, nullptr, qo, dso, workspace, dev.num_cus, stream);
     return run_tiles(kOutQ8, false, qa, ds, M, qs, sm, N, K, nullptr, nullptr, qo, dso, workspace,
                      dev.num_cus, stream);

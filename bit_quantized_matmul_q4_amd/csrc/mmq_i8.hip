@@ -150,11 +150,15 @@ __global__ __launch_bounds__(256) void k_mmqi_prep(const int8_t *__restrict__ qa
     }
 }
 
-// y (row stride ldy) for activation rows [0, M) and weight rows [0, N);
-// rec / smrec from k_mmqi_prep (Mp, Np: M and N padded to whole tiles).
+// y (row stride ldy) for activation rows [0, M) and weight rows [0, N), or
+// with kQ8 y quantized to Q8_1 along n (qo int8 [M][ldy], dso [M][ldy/32]) as
+// q8_1_quantize would do it; rec / smrec from k_mmqi_prep (Mp, Np: M and N
+// padded to whole tiles).
+template <bool kQ8>
 __global__ __launch_bounds__(kPThreads, 2) void k_mmqi(const int8_t *__restrict__ qa, const uint8_t *__restrict__ qs,
                                                        const uint32_t *__restrict__ rec,
                                                        const float2 *__restrict__ smrec, float *__restrict__ y,
+                                                       int8_t *__restrict__ qo, uint32_t *__restrict__ dso,
                                                        int M, int N, int K, int Mp, int Np, int tiles_m,
                                                        int64_t ldy, int vec_store)
 {
@@ -372,7 +376,41 @@ __global__ __launch_bounds__(kPThreads, 2) void k_mmqi(const int8_t *__restrict_
 
     // ---- y: lane (l32, half) holds column m = l32 of each tile, rows 8 q + 4 half + r ----
     const int m = m0 + (int)mrow;
-    if (m < M) {
+    if constexpr (kQ8) {
+        // each 32-row tile of the lane's column is one Q8_1 block along n:
+        // 16 values here, 16 in lane ^ 32; the same fp32 decisions as
+        // q8_1_quantize (N is a multiple of 32, so a block is wholly inside
+        // or outside [0, N))
+#pragma unroll
+        for (int ta = 0; ta < 2; ++ta) {
+            const int nb = n0 + wn * 64 + ta * 32;
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(yacc[ta][e]));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const uint16_t d16 = q8_1_scale(amax);
+            const float df = f16_bits_to_f32(d16), rdf = q8_1_rcp(df);
+            int sum = 0;
+            uint32_t packed[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                packed[q] = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int a = q8_1_code(yacc[ta][4 * q + r], df, rdf);
+                    sum += a;
+                    packed[q] |= ((uint32_t)a & 0xFFu) << (8 * r);
+                }
+            }
+            sum += __shfl_xor(sum, 32);
+            if (m < M && nb < N) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint32_t *>(qo + (int64_t)m * ldy + nb + 8 * q + 4 * half) = packed[q];
+                if (half == 0) dso[(int64_t)m * (ldy / kBlock) + nb / kBlock] = q8_1_ds(d16, df, sum);
+            }
+        }
+    } else if (m < M) {
 #pragma unroll
         for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
@@ -414,7 +452,7 @@ size_t mmqi_workspace_bytes(int64_t M, int64_t N, int64_t K)
 }
 
 hipError_t launch_mmqi(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs, const uint16_t *sm,
-                       int64_t N, int K, float *y, void *workspace, hipStream_t stream)
+                       int64_t N, int K, float *y, int8_t *qo, uint16_t *dso, void *workspace, hipStream_t stream)
 {
     const int G = K / kGroup;
     const int64_t Mp = round_up_i(M, kPm), Np = round_up_i(N, kPn);
@@ -429,9 +467,17 @@ hipError_t launch_mmqi(const int8_t *qa, const uint16_t *ds, int64_t M, const ui
     if (e != hipSuccess) return e;
     const int tiles_m = (int)(Mp / kPm);
     const int64_t tiles = (int64_t)tiles_m * (Np / kPn);
-    const int vec_store = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
-    hipLaunchKernelGGL(k_mmqi, dim3((unsigned)tiles), dim3(kPThreads), 0, stream, qa, qs, rec, smrec, y, (int)M,
-                       (int)N, K, (int)Mp, (int)Np, tiles_m, (int64_t)N, vec_store);
+    if (y) {
+        const int vec_store = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+        hipLaunchKernelGGL(k_mmqi<false>, dim3((unsigned)tiles), dim3(kPThreads), 0, stream, qa, qs, rec, smrec, y,
+                           (int8_t *)nullptr, (uint32_t *)nullptr, (int)M, (int)N, K, (int)Mp, (int)Np, tiles_m,
+                           (int64_t)N, vec_store);
+    } else {
+        // Q8_1 output (N a multiple of 32)
+        hipLaunchKernelGGL(k_mmqi<true>, dim3((unsigned)tiles), dim3(kPThreads), 0, stream, qa, qs, rec, smrec,
+                           (float *)nullptr, qo, reinterpret_cast<uint32_t *>(dso), (int)M, (int)N, K, (int)Mp,
+                           (int)Np, tiles_m, (int64_t)N, 0);
+    }
     return hipGetLastError();
 }
 

@@ -35,12 +35,14 @@ hipError_t launch_gemv(const float *x, int M, const uint8_t *qs, const uint16_t 
 size_t mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // the int8 matrix-core design on its own, at any shape
 size_t mmq_int8_workspace_bytes(int64_t M, int64_t N, int64_t K);
-// pipelined int8 kernels (mmq_i8.hip) for grids of 128 x 256 tiles: shape
-// limits, workspace (per-row and per-weight-row records) and launch
+// pipelined int8 kernels (mmq_i8.hip) for grids of 128 x 128 tiles: shape
+// limits, workspace (per-row and per-weight-row records) and launch; fp32 y,
+// or with y null Q8_1 output into qo / dso (N a multiple of 32)
 bool mmqi_supported(int64_t M, int64_t N, int64_t K);
 size_t mmqi_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mmqi(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs, const uint16_t *sm,
-                       int64_t N, int K, float *y, void *workspace, hipStream_t stream);
+                       int64_t N, int K, float *y, int8_t *qo, uint16_t *dso, void *workspace,
+                       hipStream_t stream);
 hipError_t launch_mmq_int8(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
                            const uint16_t *sm, int64_t N, int K, float *y, void *workspace,
                            const DeviceInfo &dev, hipStream_t stream);

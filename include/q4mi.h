@@ -220,7 +220,9 @@ size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   - fp16 matrix cores, for grids of 256 x 128 output tiles that keep every
  *     CU evenly busy (at least 128 tiles, and at most 256 or rounds of 256
  *     at least 80 % full; e.g. M = 2048 at N = 4096 or 12288, M = 512 at
- *     N = 9216): a prep pass writes each activation as fp16(d * a * 2^f[m]),
+ *     N = 9216), unless the int8 design's 128 x 128 tiles fill the CUs in
+ *     one round (at most 256 tiles; e.g. M = 1024 at N = 4096): a prep pass
+ *     writes each activation as fp16(d * a * 2^f[m]),
  *     one power of two per row so that the largest is below 2^15; the GEMM
  *     turns each weight into fp16((scale * q + minimum) * 2^e[n]) in one
  *     fused multiply-add, one power of two per weight row so that the

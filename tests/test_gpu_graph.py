@@ -28,7 +28,7 @@ def test_graph_replays_match_eager(q4):
     qs2, sm2 = q4.q4_pack(w(512, 4096))
     qs3, sm3 = q4.q4_pack(w(224, 2048))
     qs4, sm4 = q4.q4_pack(w(12288, 512))      # fp16 design, fused row factors
-    qs5, sm5 = q4.q4_pack(w(8192, 4096))      # fp16 design, separate row-factor pass
+    qs5, sm5 = q4.q4_pack(w(9216, 4096))      # fp16 design, separate row-factor pass
     g1, gs1 = q4.q4_pack_g32(w(6144, 2560))
     g4, gs4 = q4.q4_pack_g32(w(12288, 512))
     xa = torch.empty((100, 2048), device=dev)
@@ -53,8 +53,8 @@ def test_graph_replays_match_eager(q4):
     qaf5 = torch.empty((512, 4096), dtype=torch.int8, device=dev)
     dsf5 = torch.empty((512, 128, 2), dtype=torch.float16, device=dev)
     yf = torch.empty((300, 12288), device=dev)
-    yf5 = torch.empty((512, 8192), device=dev)
-    yi5 = torch.empty((512, 8192), device=dev)
+    yf5 = torch.empty((512, 9216), device=dev)
+    yi5 = torch.empty((512, 9216), device=dev)
     qof = torch.empty((300, 12288), dtype=torch.int8, device=dev)
     dsof = torch.empty((300, 384, 2), dtype=torch.float16, device=dev)
     yg1 = torch.empty((1, 6144), device=dev)
@@ -63,8 +63,8 @@ def test_graph_replays_match_eager(q4):
     ygf = torch.empty((300, 12288), device=dev)
     qs3g, sm3g = q4.q4_pack_g32(w(224, 2048))
     ws_f = torch.empty((q4.q4_mmq_workspace_bytes(300, 12288, 512),), dtype=torch.uint8, device=dev)
-    ws_f5 = torch.empty((q4.q4_mmq_workspace_bytes(512, 8192, 4096),), dtype=torch.uint8, device=dev)
-    ws_i5 = torch.empty((max(q4.q4_mmq_int8_workspace_bytes(512, 8192, 4096), 1),), dtype=torch.uint8, device=dev)
+    ws_f5 = torch.empty((q4.q4_mmq_workspace_bytes(512, 9216, 4096),), dtype=torch.uint8, device=dev)
+    ws_i5 = torch.empty((max(q4.q4_mmq_int8_workspace_bytes(512, 9216, 4096), 1),), dtype=torch.uint8, device=dev)
     ws_g8 = torch.empty((max(q4.q4_gemv_g32_workspace_bytes(8, 6144, 2560), 1),), dtype=torch.uint8, device=dev)
     # the fp16 design's workspace holds its activation image (2 K bytes per
     # row, rows padded to 256, plus 4 bytes per row) and 8 bytes per weight
@@ -72,8 +72,8 @@ def test_graph_replays_match_eager(q4):
     # int8 kernels where those exceed it; q4_mmq_gemm_int8 has its own (the
     # per-row and per-weight-row records of its pipelined kernel)
     assert q4.q4_mmq_workspace_bytes(300, 12288, 512) == 512 * (2 * 512 + 4) + 12288 * 8
-    assert q4.q4_mmq_workspace_bytes(512, 8192, 4096) >= 512 * (2 * 4096 + 4) + 8192 * 8
-    assert q4.q4_mmq_int8_workspace_bytes(512, 8192, 4096) == 512 * 16 * 32 + 8192 * 16 * 8
+    assert q4.q4_mmq_workspace_bytes(512, 9216, 4096) >= 512 * (2 * 4096 + 4) + 9216 * 8
+    assert q4.q4_mmq_int8_workspace_bytes(512, 9216, 4096) == 512 * 16 * 32 + 9216 * 16 * 8
     # the shapes take the K-split paths (partials and a second, summing kernel)
     assert q4.q4_mmq_workspace_bytes(100, 224, 2048) > 0
     assert q4.q4_gemv_workspace_bytes(8, 512, 4096) > 0

@@ -396,6 +396,27 @@ def test_mmq_pp1024_gate_up(q4, orc):
     mmq_check(q4, orc, M, c["N"], c["K"], c["seed"], True, "mmq pp1024 gate_up")
 
 
+@pytest.mark.parametrize("M,N,K", [(1024, 4096, 12288), (640, 6144, 4096)])
+def test_mmq_one_round_int8_route(q4, orc, M, N, K):
+    # grids whose 128 x 128 tiles fill the CUs in one round (256 and 240
+    # tiles) while the fp16 design's 256 x 128 tiles would leave about half
+    # of them idle: the fp32 route takes the pipelined integer kernel (its
+    # per-row records in the workspace); the prefill sweep's pp = 1024 point
+    # on the 12288 -> 4096 layer is the first shape (256 sampled rows)
+    assert q4.q4_mmq_workspace_bytes(M, N, K) >= q4.q4_mmq_int8_workspace_bytes(M, N, K) > 0
+    rows = np.sort(np.random.default_rng(M + N).choice(M, size=256, replace=False))
+    say("mmq one-round int8 route M=%d N=%d K=%d (256 sampled rows)" % (M, N, K))
+    W, x = wl.mmq_case(M + K, M, N, K, True)
+    qs, sm = q4.q4_pack(dev(W))
+    qa, ds = q4.q8_1_quantize(dev(x))
+    y = q4.q4_mmq_gemm(qa, ds, qs, sm)
+    assert torch.equal(y, q4.q4_mmq_gemm_int8(qa, ds, qs, sm))
+    qa_h = qa.cpu().numpy()
+    ds_h = ds.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = orc.q4_mmq(qa_h[rows], ds_h[rows], qs.cpu().numpy(), sm.cpu().view(torch.int16).numpy().view(np.uint16), K)
+    close(y.cpu().numpy()[rows], ref, "mmq one-round int8 %dx%dx%d" % (M, N, K))
+
+
 INT8_FULL = [dict(wl.MMQ_512, name="m512")] + wl.MMQ_2048
 
 
@@ -467,11 +488,15 @@ def test_mmq_long_k(q4, orc):
     mmq_check(q4, orc, 130, 100, 65792, 77, True, "mmq long K")
 
 
-@pytest.mark.parametrize("M,N,K,seed", [(100, 224, 512, 61), (100, 224, 2048, 62), (512, 9216, 2560, 0)])
+@pytest.mark.parametrize("M,N,K,seed", [(100, 224, 512, 61), (100, 224, 2048, 62), (512, 9216, 2560, 0),
+                                        (600, 6144, 4096, 63), (1024, 4096, 12288, 64),
+                                        (1024, 12288, 4096, 65)])
 def test_mmq_q8_1_output_bit_exact(q4, orc, M, N, K, seed):
     # the Q8_1-producing epilogue equals quantizing the fp32 GEMM result, bit
     # for bit (K = 2048 at 2 tiles takes the K-split path, whose sum pass
-    # quantizes); and the oracle's quantizer on that fp32 result agrees too
+    # quantizes; the last three shapes, 240, 256 and 768 tiles of 128 x 128,
+    # the pipelined integer kernel's epilogue, the first with ragged rows);
+    # and the oracle's quantizer on that fp32 result agrees too
     say("mmq -> Q8_1 M=%d N=%d K=%d" % (M, N, K))
     W, x = wl.mmq_case(seed, M, N, K, True)
     qs, sm = q4.q4_pack(dev(W))
