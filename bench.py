@@ -70,6 +70,25 @@ def q8_bytes(M, K):
     return M * K * 4 + M * K + M * (K // 32) * 4
 
 
+# Figures timed outside the step first run their launch back to back for this
+# long (discarded): the GPU's clocks ramp on a millisecond scale, and a few
+# warm calls after an idle moment leave the timed launches mid-ramp (tiny-M
+# M = 8 measured 82 us after 1.5 s idle and 5 ms of calls, 62 us after 20 ms).
+SUSTAIN_MS = 100.0
+
+
+def sustain(fn, ms=SUSTAIN_MS):
+    """Call fn(i) back to back for at least ms of wall time (warm-up)."""
+    import torch
+    torch.cuda.synchronize()
+    t0, i = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,7 +241,8 @@ def cpu_baseline(wl):
 def tiny_m_sweep(q4, wl, dev, stream, reps=12):
     """GEMV at M = 1..16 on the lm_head shape (K=4096, N=151936), outside the
     timed step: two weight copies (2 x 321 MB) alternate so the Infinity Cache
-    cannot serve them; median of per-launch HIP-event times."""
+    cannot serve them; after the sustained warm-up, median of per-launch
+    HIP-event times."""
     import torch
     c = wl.TINY_M
     K, N = c["K"], c["N"]
@@ -238,8 +258,7 @@ def tiny_m_sweep(q4, wl, dev, stream, reps=12):
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
         ws_n = q4.q4_gemv_workspace_bytes(M, N, K)
         ws = torch.empty((max(ws_n, 1),), dtype=torch.uint8, device=dev)
-        for i in range(6):  # three warm calls per weight copy
-            q4.q4_gemv(x, *copies[i % 2], y=y, workspace=ws)
+        sustain(lambda i: q4.q4_gemv(x, *copies[i % 2], y=y, workspace=ws))
         times = []
         for r in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -257,13 +276,14 @@ def tiny_m_sweep(q4, wl, dev, stream, reps=12):
 
 
 def graph_launch_us(fn, n, stream):
-    """Median per-launch time (us) of n launches captured by fn() into one graph."""
+    """Median per-launch time (us) of n launches captured by fn() into one graph
+    (replayed for the sustained warm-up first)."""
     import torch
     fn()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fn()
-    torch.cuda.synchronize()
+    sustain(lambda i: g.replay())
     times = []
     for _ in range(5):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -340,8 +360,7 @@ def vendor_gemm(wl, dev, stream, reps=10):
         bi = torch.randint(-8, 8, (K, N), generator=g, device=dev, dtype=torch.int8)
         res = {}
         for name, fn in (("f16_mm", lambda: torch.mm(a, b)), ("i8_int_mm", lambda: torch._int_mm(ai, bi))):
-            for _ in range(3):
-                fn()
+            sustain(lambda i: fn(), ms=30.0)
             ev = []
             for _ in range(reps):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -360,11 +379,12 @@ def prefill_sweep(q4, wl, dev, stream):
     """MMQ (with and without its Q8_1 pass) at pp = 256..2048 on the ~9B-shaped
     layer pair, and the GEMV/MMQ crossover at M = 16..256 on the 4096 -> 12288
     layer: the GEMV path runs ceil(M/16) launches of 16 rows, the MMQ path
-    Q8_1 + MMQ.  Median of 5 event-timed repetitions each."""
+    Q8_1 + MMQ.  Median of 5 event-timed repetitions each, after 30 ms of
+    back-to-back calls."""
     import torch
 
     def timed(fn, reps=5):
-        fn()
+        sustain(lambda i: fn(), ms=30.0)
         ts = []
         for _ in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -436,8 +456,7 @@ def group32_figures(q4, wl, dev, stream):
     import torch
 
     def timed(fn, reps=12):
-        for r in range(4):  # warm calls, both weight copies
-            fn(r)
+        sustain(fn)  # both weight copies in turn
         ts = []
         for r in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
