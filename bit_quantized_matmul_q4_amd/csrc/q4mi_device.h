@@ -146,24 +146,31 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // go to LDS byte address base + 16 i (4 i); soff and base are the same for the
 // whole wave.  Written as asm so that the compiler neither tracks nor waits
 // for them: a kernel orders them itself (s_waitcnt vmcnt before the barrier
-// that publishes the LDS data).  No registers are written.  Bytes outside the
+// that publishes the LDS data).  No vector registers are written; M0 (the LDS
+// base of the load) is saved in a scratch SGPR and restored, so the compiler's
+// own use of M0, if any, is undisturbed, and one wait state separates the
+// SALU write of M0 from the load that reads it.  Bytes outside the
 // descriptor's range arrive as zeros.
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t base)
 {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-                 :
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %4 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
                  : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(base)),
                    "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "memory", "m0");
+                 : "memory");
 }
 
 __device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t base)
 {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, %3 offen lds"
-                 :
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %4 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
                  : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(base)),
                    "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "memory", "m0");
+                 : "memory");
 }
 
 // Wait until at most kN vector-memory loads of this wave are outstanding,
