@@ -27,7 +27,7 @@ block dots); each is reported against its own matrix-core peak.  For context
 only, "vendor_gemm" times the vendor BLAS's plain GEMMs (torch.mm on fp16,
 torch._int_mm on int8 operands, no quantization scales) at the same shapes.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--sustain-ms T]
        python bench.py --pmc-mmq        (Q8_1 + MMQ, M=2048 4096->12288, 3 launches;
                                          nothing printed)
        python bench.py --pmc-mmq-int8   (the same through q4_mmq_gemm_int8)
@@ -75,11 +75,18 @@ def q8_bytes(M, K):
 # warm calls after an idle moment leave the timed launches mid-ramp (tiny-M
 # M = 8 measured 82 us after 1.5 s idle and 5 ms of calls, 62 us after 20 ms).
 SUSTAIN_MS = 100.0
+_SUSTAIN_SCALE = [1.0]  # --sustain-ms / SUSTAIN_MS (shorter under a profiler)
+
+
+def log(msg):
+    """Progress line on stderr (stdout carries only the JSON line)."""
+    print("bench: " + msg, file=sys.stderr, flush=True)
 
 
 def sustain(fn, ms=SUSTAIN_MS):
     """Call fn(i) back to back for at least ms of wall time (warm-up)."""
     import torch
+    ms *= _SUSTAIN_SCALE[0]
     torch.cuda.synchronize()
     t0, i = time.perf_counter(), 0
     while (time.perf_counter() - t0) * 1e3 < ms:
@@ -95,6 +102,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sustain-ms", type=float, default=SUSTAIN_MS,
+                    help="warm-up of each figure timed outside the step (shorter for profiled runs)")
     ap.add_argument("--no-graph", action="store_true", help="launch the decode layers one by one")
     ap.add_argument("--no-tiny-m", action="store_true", help="skip the tiny-M GEMV sweep")
     ap.add_argument("--no-prefill-sweep", action="store_true",
@@ -376,7 +385,8 @@ def vendor_gemm(wl, dev, stream, reps=10):
 
 
 def prefill_sweep(q4, wl, dev, stream):
-    """MMQ (with and without its Q8_1 pass) at pp = 256..2048 on the ~9B-shaped
+    """MMQ (with and without its Q8_1 pass; q4_mmq_gemm as routed and, under
+    "int8_design", q4_mmq_gemm_int8) at pp = 256..2048 on the ~9B-shaped
     layer pair, and the GEMV/MMQ crossover at M = 16..256 on the 4096 -> 12288
     layer: the GEMV path runs ceil(M/16) launches of 16 rows, the MMQ path
     Q8_1 + MMQ.  Median of 5 event-timed repetitions each, after 30 ms of
@@ -413,10 +423,15 @@ def prefill_sweep(q4, wl, dev, stream):
             y = torch.empty((pp, N), dtype=torch.float32, device=dev)
             q8_us = timed(lambda: q4.q8_1_quantize(x, qa, ds))
             mmq_us = timed(lambda: q4.q4_mmq_gemm(qa, ds, qs, sm, y=y))
+            wi = torch.empty((max(1, q4.q4_mmq_int8_workspace_bytes(pp, N, K)),), dtype=torch.uint8, device=dev)
+            int8_us = timed(lambda: q4.q4_mmq_gemm_int8(qa, ds, qs, sm, y=y, workspace=wi))
             ops = 2.0 * pp * N * K
             row[c["name"]] = {"mmq_us": round(mmq_us, 1), "q8_1_us": round(q8_us, 1),
                               "tops": round(ops / (mmq_us * 1e-6) / 1e12, 1),
-                              "tops_incl_q8_1": round(ops / ((mmq_us + q8_us) * 1e-6) / 1e12, 1)}
+                              "tops_incl_q8_1": round(ops / ((mmq_us + q8_us) * 1e-6) / 1e12, 1),
+                              "int8_design": {"us": round(int8_us, 1),
+                                              "tops": round(ops / (int8_us * 1e-6) / 1e12, 1),
+                                              "frac_i8_peak": round(ops / (int8_us * 1e-6) / 1e12 / I8_PEAK_TOPS, 4)}}
             # handing the result on as Q8_1 (the next layer's input): quantizing
             # in the GEMM epilogue vs the GEMM then a separate Q8_1 pass over y
             qo = torch.empty((pp, N), dtype=torch.int8, device=dev)
@@ -514,6 +529,7 @@ def main():
     import bit_quantized_matmul_q4_amd as q4
     from bit_quantized_matmul_q4_amd import workloads as wl
 
+    _SUSTAIN_SCALE[0] = args.sustain_ms / SUSTAIN_MS
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -623,6 +639,7 @@ def main():
             i += 4
         return ev
 
+    log("setup done; warm-up steps")
     for _ in range(args.warmup):
         step([E() for _ in range(n_ev)])
     cp_dst.copy_(cp_src)
@@ -719,6 +736,7 @@ def main():
                 "achieved": big["int8_design"]["tops"], "peak": I8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": big["int8_design"]["frac_i8_peak"]}),
     }
+    log("timed steps done")
     n_unfused = LAYERS * len(layers[0])
     unf_us = graph_launch_us(decode_layers_unfused, n_unfused, stream) * n_unfused
     out["decode_unfused"] = {
@@ -732,12 +750,16 @@ def main():
     out["decode_projections_fused"] = decode_breakdown(q4, fused_layers, xs, stream)
     out["graph_launch_floor_us"] = launch_floor_us(stream)
     out["gemv_single_4096"] = single_gemv(q4, wl, dev, stream)
+    log("decode breakdown done")
     if not args.no_tiny_m:
         out["gemv_tiny_m"] = tiny_m_sweep(q4, wl, dev, stream)
+        log("tiny-M sweep done")
     if not args.no_prefill_sweep:
         out["prefill_sweep"] = prefill_sweep(q4, wl, dev, stream)
+        log("prefill sweep done")
     out["group32"] = group32_figures(q4, wl, dev, stream)
     out["vendor_gemm"] = vendor_gemm(wl, dev, stream)
+    log("group-32 and vendor GEMM done")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
