@@ -61,6 +61,11 @@ constexpr int kFm = 256;           // activation rows per tile
 constexpr int kFn = 128;           // weight rows per tile
 constexpr int kFk = 64;            // K per step: two Q8_1 blocks
 constexpr int kFThreads = 256;
+// K steps per image workgroup: two (128 B of a row per thread, whole cache
+// lines) while that still leaves kImgMinGroups workgroups, else one
+constexpr int kImgMaxSteps = 2;
+constexpr int kImgMinGroups = 256;
+static_assert(kGroup % (kFk * kImgMaxSteps) == 0, "K (a multiple of 256) holds whole image workgroups");
 constexpr int kStepVecs = 8 * kFm; // 16-byte vectors of the image per (tile, step)
 // Computing waves (one per SIMD) and the 32-row activation tiles each owns.
 // Eight computing waves (two per SIMD, 64 x 64 each, 129 registers) were
@@ -130,9 +135,11 @@ __device__ __forceinline__ int weight_exponent(float wmax)
     return 0;
 }
 
-// The fp16 activation image of one (256-row tile mt, K step s): thread r
-// converts row mt * 256 + r, k in [64 s, 64 s + 64).  Vector (t, h, r) of the
-// step (t = 0..3 MFMA of the step, h = Q8_1 block of the step) holds
+// The fp16 activation image of one 256-row tile mt and kSteps K steps s0,
+// s0 + 1, ...: thread r converts row mt * 256 + r, k in [64 s0, 64 s0 +
+// 64 kSteps) (with two steps, whole 128-byte lines of its row).
+// Vector (t, h, r) of step s (t = 0..3 MFMA of the step, h = Q8_1 block of
+// the step) holds
 // x'[k] for k = 64 s + 32 h + {4t, 4t+2, 16+4t, 18+4t, 4t+1, 4t+3, 17+4t, 19+4t}:
 // the order in which the GEMM unpacks one 32-bit word of packed weights.
 // kRowScale: each thread also finds its row's factor itself (all the row's
@@ -143,7 +150,7 @@ __device__ __forceinline__ int weight_exponent(float wmax)
 // weight row's exponent E (weight_exponent over its P pairs) for rows [0,
 // Np), Np = N rounded up to whole 128-row tiles: wexp[n] = (E, 2^-E as fp32
 // bits), (0, 1.0) past N.
-template <bool kRowScale>
+template <bool kRowScale, int kSteps>
 __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restrict__ qa,
                                                           const uint32_t *__restrict__ ds,
                                                           float *__restrict__ fs, int M, int K,
@@ -173,19 +180,19 @@ __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restri
         }
         return;
     }
-    const int s = blockIdx.x, mt = blockIdx.y, r = threadIdx.x;
+    const int s0 = blockIdx.x * kSteps, mt = blockIdx.y, r = threadIdx.x;
     const int S = K / kFk;
     const int m = mt * kFm + r;
-    uint4 q[4] = {};
-    uint32_t dw[2] = {0, 0};
+    uint4 q[4 * kSteps] = {};
+    uint32_t dw[2 * kSteps] = {};
     float F = 1.0f;
     if (m < M) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(qa + (int64_t)m * K + (int64_t)s * kFk);
+        const uint4 *src = reinterpret_cast<const uint4 *>(qa + (int64_t)m * K + (int64_t)s0 * kFk);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = src[i];
-        const uint32_t *dp = ds + (int64_t)m * (K / kBlock) + 2 * s;
-        dw[0] = dp[0];
-        dw[1] = dp[1];
+        for (int i = 0; i < 4 * kSteps; ++i) q[i] = src[i];
+        const uint32_t *dp = ds + (int64_t)m * (K / kBlock) + 2 * s0;
+#pragma unroll
+        for (int i = 0; i < 2 * kSteps; ++i) dw[i] = dp[i];
         if (kRowScale) {
             const int B4 = K / kBlock / 4;  // 16-byte vectors of the row's (d, s) pairs
             const uint4 *p = reinterpret_cast<const uint4 *>(ds + (int64_t)m * (K / kBlock));
@@ -199,30 +206,33 @@ __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restri
                     dm = max(dm, max(max(v[u].x & 0x7FFFu, v[u].y & 0x7FFFu), max(v[u].z & 0x7FFFu, v[u].w & 0x7FFFu)));
             }
             F = row_factor(dm);
-            if (s == 0) fs[m] = F;
+            if (s0 == 0) fs[m] = F;
         } else {
             F = fs[m];
         }
     }
-    uint4 *dst = img + ((int64_t)mt * S + s) * kStepVecs + r;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const float df = f16_bits_to_f32(dw[h] & 0xFFFFu) * F;  // exact: F is a power of two
-        const uint32_t w8[8] = {q[2 * h].x, q[2 * h].y, q[2 * h].z, q[2 * h].w,
-                                q[2 * h + 1].x, q[2 * h + 1].y, q[2 * h + 1].z, q[2 * h + 1].w};
-        // d * a is exact in fp32 (11 x 7 bits); one rounding to fp16
-        auto cv = [&](uint32_t w, int byte) -> uint32_t {
-            return f32_to_f16_bits(df * (float)(int8_t)(w >> (8 * byte)));
-        };
+    for (int ss = 0; ss < kSteps; ++ss) {
+        uint4 *dst = img + ((int64_t)mt * S + s0 + ss) * kStepVecs + r;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint32_t lo = w8[t], hi = w8[t + 4];
-            uint4 o;
-            o.x = cv(lo, 0) | (cv(lo, 2) << 16);
-            o.y = cv(hi, 0) | (cv(hi, 2) << 16);
-            o.z = cv(lo, 1) | (cv(lo, 3) << 16);
-            o.w = cv(hi, 1) | (cv(hi, 3) << 16);
-            dst[(2 * t + h) * kFm] = o;
+        for (int h = 0; h < 2; ++h) {
+            const float df = f16_bits_to_f32(dw[2 * ss + h] & 0xFFFFu) * F;  // exact: F is a power of two
+            const uint4 *qh = q + 4 * ss + 2 * h;
+            const uint32_t w8[8] = {qh[0].x, qh[0].y, qh[0].z, qh[0].w, qh[1].x, qh[1].y, qh[1].z, qh[1].w};
+            // d * a is exact in fp32 (11 x 7 bits); one rounding to fp16
+            auto cv = [&](uint32_t w, int byte) -> uint32_t {
+                return f32_to_f16_bits(df * (float)(int8_t)(w >> (8 * byte)));
+            };
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t lo = w8[t], hi = w8[t + 4];
+                uint4 o;
+                o.x = cv(lo, 0) | (cv(lo, 2) << 16);
+                o.y = cv(hi, 0) | (cv(hi, 2) << 16);
+                o.z = cv(lo, 1) | (cv(lo, 3) << 16);
+                o.w = cv(hi, 1) | (cv(hi, 3) << 16);
+                dst[(2 * t + h) * kFm] = o;
+            }
         }
     }
 }
@@ -598,16 +608,18 @@ hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const ui
         // row-scale reads they repeat (each step re-reads its rows' scales)
         // stay within kFusedScaleBytes and the scales allow 16-byte loads;
         // otherwise a separate pass
+        const bool two = (int64_t)(S / kImgMaxSteps) * tiles_m >= kImgMinGroups;
+        const dim3 igrid((unsigned)(two ? S / kImgMaxSteps : S), (unsigned)(tiles_m + 1));
         if (mp * S * B * 4 <= kFusedScaleBytes && (reinterpret_cast<uintptr_t>(ds) & 15) == 0) {
-            hipLaunchKernelGGL(k_mmqf_image<true>, dim3((unsigned)S, (unsigned)(tiles_m + 1)), dim3(kFThreads), 0,
-                               stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm, K, img, sm32, (int)N, P,
-                               (int)npad, wexp);
+            auto kimg = two ? k_mmqf_image<true, kImgMaxSteps> : k_mmqf_image<true, 1>;
+            hipLaunchKernelGGL(kimg, igrid, dim3(kFThreads), 0, stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm,
+                               K, img, sm32, (int)N, P, (int)npad, wexp);
         } else {
             hipLaunchKernelGGL(k_mmqf_rowscale, dim3((unsigned)(mp / 4)), dim3(256), 0, stream, ds32 + m0 * B,
                                (int)mm, B, (int)mp, fs);
-            hipLaunchKernelGGL(k_mmqf_image<false>, dim3((unsigned)S, (unsigned)(tiles_m + 1)), dim3(kFThreads), 0,
-                               stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm, K, img, sm32, (int)N, P,
-                               (int)npad, wexp);
+            auto kimg = two ? k_mmqf_image<false, kImgMaxSteps> : k_mmqf_image<false, 1>;
+            hipLaunchKernelGGL(kimg, igrid, dim3(kFThreads), 0, stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm,
+                               K, img, sm32, (int)N, P, (int)npad, wexp);
         }
         for (int64_t n0 = 0; n0 < N; n0 += n_max) {
             const int64_t nn = N - n0 < n_max ? N - n0 : n_max;
