@@ -31,6 +31,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [
        python bench.py --pmc-mmq        (Q8_1 + MMQ, M=2048 4096->12288, 3 launches;
                                          nothing printed)
        python bench.py --pmc-mmq-int8   (the same through q4_mmq_gemm_int8)
+       python bench.py --pmc-tiny-m M   (tiny-M GEMV at M rows, two weight copies in turn,
+                                         4 launches)
        python bench.py --pmc-workload   (lm_head GEMV over two weight copies in turn,
                                          4 launches, and a 256 MiB copy, 3 launches,
                                          for hardware-counter runs; prints nothing)
@@ -114,6 +116,9 @@ def parse():
                     help="only launch Q8_1 + MMQ on the M=2048, 4096 -> 12288 layer, 3 times (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-mmq-int8", action="store_true",
                     help="as --pmc-mmq through q4_mmq_gemm_int8 (the int8 matrix-core design)")
+    ap.add_argument("--pmc-tiny-m", type=int, default=0, metavar="M",
+                    help="only launch the tiny-M GEMV (K=4096, N=151936) at M rows, 4 times over two "
+                         "weight copies in turn (for rocprofv3 --pmc)")
     return ap.parse_args()
 
 
@@ -190,6 +195,29 @@ def pmc_mmq(int8=False):
     for _ in range(3):
         qa, ds = q4.q8_1_quantize(x)
         gemm(qa, ds, qs, sm, y=y)
+    torch.cuda.synchronize()
+
+
+def pmc_tiny_m(M):
+    """The tiny-M GEMV (K = 4096, N = 151936) at M rows x4, alternating two
+    weight copies (642 MB together, beyond the Infinity Cache); nothing timed
+    or printed."""
+    import torch
+    import bit_quantized_matmul_q4_amd as q4
+    from bit_quantized_matmul_q4_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    c = wl.TINY_M
+    K, N = c["K"], c["N"]
+    copies = []
+    for i in range(2):
+        W = wl.draw_weights(wl.generator(c["seed"] + 100 * i, dev), N, K, dev)
+        copies.append(q4.q4_pack(W))
+        del W
+    x = wl.draw_activations(wl.generator(M, dev), M, K, False, dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = torch.empty((max(1, q4.q4_gemv_workspace_bytes(M, N, K)),), dtype=torch.uint8, device=dev)
+    for i in range(4):
+        q4.q4_gemv(x, *copies[i % 2], y=y, workspace=ws)
     torch.cuda.synchronize()
 
 
@@ -520,6 +548,9 @@ def main():
         sys.exit(2)
     if args.pmc_mmq or args.pmc_mmq_int8:
         pmc_mmq(int8=args.pmc_mmq_int8)
+        return
+    if args.pmc_tiny_m:
+        pmc_tiny_m(args.pmc_tiny_m)
         return
     if args.pmc_workload:
         pmc_workload()
