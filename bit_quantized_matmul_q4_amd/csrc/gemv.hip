@@ -769,9 +769,15 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
             const float *fg = fac + cg * F;
             const float4 f = *reinterpret_cast<const float4 *>(fg + 4 * kq);
             if (kG32) {
-                // one MFMA per run, each with its own (scale, minimum); two
-                // accumulators so a run's epilogue overlaps the next product
+                // one MFMA per run, each with its own (scale, minimum): the
+                // group's T = sum over runs of scale * dot on the VALU (two
+                // accumulators so a run's scaling overlaps the next product),
+                // its minimum and correction terms sum over runs of (c scale +
+                // X minimum) as four fp32 MFMAs of rank 2 accumulating into y
+                // (A[m][k] = c or X of run 2q + k/2 for row m, B[k][n] = scale
+                // or minimum of that run for row n), then y += f T
                 float4_t accs[2];
+                float4_t T = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int d = 0; d < 8; ++d) {
                     const half8_t a = *reinterpret_cast<const half8_t *>(ag + d * 4 * MP * 16);
@@ -782,29 +788,31 @@ __global__ __launch_bounds__(kBThreads) void k_gemv_mfma(const float *__restrict
                     const half8_t b = __builtin_bit_cast(half8_t, uint4{p[0], p[1], p[2], p[3]});
                     accs[d & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     if (d > 0) {
-                        const int dp = d - 1;
-                        const float4_t acc = accs[dp & 1];
-                        const uint32_t sv = tile_sm[j * 8 + dp];
-                        const float sf = f16_bits_to_f32(sv & 0xFFFFu), mf = f16_bits_to_f32(sv >> 16);
-                        const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + dp * kBRows + 4 * kq);
-                        const float4 cc = *reinterpret_cast<const float4 *>(fg + 9 * kBRows + dp * kBRows + 4 * kq);
-                        yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
-                        yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
-                        yacc[2] = fmaf(sf, fmaf(f.z, acc[2], cc.z), fmaf(mf, X.z, yacc[2]));
-                        yacc[3] = fmaf(sf, fmaf(f.w, acc[3], cc.w), fmaf(mf, X.w, yacc[3]));
+                        const float sf = f16_bits_to_f32(tile_sm[j * 8 + d - 1] & 0xFFFFu);
+                        const float4_t acc = accs[(d - 1) & 1];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) T[e] = fmaf(sf, acc[e], T[e]);
                     }
                 }
                 {
+                    const float sf = f16_bits_to_f32(tile_sm[j * 8 + 7] & 0xFFFFu);
                     const float4_t acc = accs[1];
-                    const uint32_t sv = tile_sm[j * 8 + 7];
-                    const float sf = f16_bits_to_f32(sv & 0xFFFFu), mf = f16_bits_to_f32(sv >> 16);
-                    const float4 X = *reinterpret_cast<const float4 *>(fg + kBRows + 7 * kBRows + 4 * kq);
-                    const float4 cc = *reinterpret_cast<const float4 *>(fg + 9 * kBRows + 7 * kBRows + 4 * kq);
-                    yacc[0] = fmaf(sf, fmaf(f.x, acc[0], cc.x), fmaf(mf, X.x, yacc[0]));
-                    yacc[1] = fmaf(sf, fmaf(f.y, acc[1], cc.y), fmaf(mf, X.y, yacc[1]));
-                    yacc[2] = fmaf(sf, fmaf(f.z, acc[2], cc.z), fmaf(mf, X.z, yacc[2]));
-                    yacc[3] = fmaf(sf, fmaf(f.w, acc[3], cc.w), fmaf(mf, X.w, yacc[3]));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) T[e] = fmaf(sf, acc[e], T[e]);
                 }
+                const int ki = lane >> 4, mi = j & (MP - 1);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int run = 2 * q + (ki >> 1);
+                    const float av = fg[((ki & 1) ? kBRows : 9 * kBRows) + run * kBRows + mi];
+                    const uint32_t sv = tile_sm[j * 8 + run];
+                    const float bv = f16_bits_to_f32((ki & 1) ? (sv >> 16) : (sv & 0xFFFFu));
+                    yacc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, yacc, 0, 0, 0);
+                }
+                yacc[0] = fmaf(f.x, T[0], yacc[0]);
+                yacc[1] = fmaf(f.y, T[1], yacc[1]);
+                yacc[2] = fmaf(f.z, T[2], yacc[2]);
+                yacc[3] = fmaf(f.w, T[3], yacc[3]);
             } else {
                 // two independent accumulator chains (even / odd steps)
                 float4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
