@@ -1,14 +1,18 @@
-"""MMQ on weight matrices beyond the 2 GiB reach of one buffer descriptor.
+"""MMQ on operands beyond the 2 GiB reach of one buffer descriptor.
 
-Every MMQ launcher addresses the packed weights through descriptors with
-32-bit offsets, so a call whose codes pass 2 GiB runs as several row ranges
-of the weights, each with its own launch.  1048576 x 4096 weights hold
-exactly 2 GiB of codes: the fp16 design and the unpipelined integer kernel
-cut them into 1048448 rows and a 128-row tail.  These tests check, against
-the CPU oracle, the outputs on both sides of that cut and at the ends (a
-sample of weight rows and activation rows; the oracle takes the sampled rows
-as a smaller problem of its own, since packing is per row), and that the
-Q8_1-output route is the fp32 route quantized bit for bit across the cut.
+Every MMQ launcher addresses its operands through descriptors with 32-bit
+offsets, so a call whose packed weights pass 2 GiB runs as several row
+ranges of the weights, each with its own launch, and one whose activations
+pass it as several row ranges of the activations.  1048576 x 4096 weights
+hold exactly 2 GiB of codes: the fp16 design and the unpipelined integer
+kernel cut them into 1048448 rows and a 128-row tail.  600000 x 4096 Q8_1
+activations run in 32768-row chunks (the fp16 design's activation image) or
+524160-row ranges (the integer kernel).  These tests check, against the CPU
+oracle, the outputs on both sides of each cut and at the ends (a sample of
+weight rows and activation rows; the oracle takes the sampled rows as a
+smaller problem of its own, since packing and Q8_1 are per row), and that
+the Q8_1-output route is the fp32 route quantized bit for bit across the
+weight cut.
 """
 import numpy as np
 import pytest
@@ -98,4 +102,37 @@ def test_mmq_g32_beyond_2gib_of_weights(q4, orc, big_case):
     close(sampled(y, c), orc.q4_mmq(c["qa_h"], c["ds_h"], qs_o, sm_o, K_BIG, group=32),
           "mmq g32 beyond 2 GiB")
     del y
+    torch.cuda.empty_cache()
+
+
+def test_mmq_beyond_2gib_of_activations(q4, orc):
+    # 600000 x 4096 Q8_1 activations (2.46 GB of codes): the fp16 design runs
+    # them in chunks of 32768 rows (its 256 MiB activation image), the
+    # unpipelined integer kernel in ranges of 524160 rows (2 GiB of codes)
+    M, N, K = 600000, 128, 4096
+    say("mmq beyond 2 GiB of activations: M=%d N=%d K=%d (sampled rows)" % (M, N, K))
+    g = wl.generator(2051, "cuda")
+    W = wl.draw_weights(g, N, K, "cuda")
+    qs, sm = q4.q4_pack(W)
+    x = wl.draw_activations(g, M, K, True, "cuda")
+    qa, ds = q4.q8_1_quantize(x)
+    del x
+    torch.cuda.empty_cache()
+    cuts = [32767, 32768, 524159, 524160]
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], cuts,
+                                     np.random.default_rng(2052).choice(M, 60, replace=False)]))
+    ridx = torch.from_numpy(rows).cuda()
+    qa_h = qa.index_select(0, ridx).cpu().numpy()
+    ds_h = ds.index_select(0, ridx).cpu().view(torch.int16).numpy().view(np.uint16)
+    qs_o, sm_o = orc.q4_pack(W.cpu().numpy())
+    assert np.array_equal(qs.cpu().numpy(), qs_o)
+    assert np.array_equal(sm.cpu().view(torch.int16).numpy().view(np.uint16), sm_o)
+    ref = orc.q4_mmq(qa_h, ds_h, qs_o, sm_o, K)
+    y = q4.q4_mmq_gemm(qa, ds, qs, sm)
+    close(y.index_select(0, ridx).cpu().numpy(), ref, "mmq routed beyond 2 GiB of activations")
+    del y
+    say("  integer design")
+    yi = q4.q4_mmq_gemm_int8(qa, ds, qs, sm)
+    close(yi.index_select(0, ridx).cpu().numpy(), ref, "mmq int8 design beyond 2 GiB of activations")
+    del yi, qa, ds
     torch.cuda.empty_cache()
