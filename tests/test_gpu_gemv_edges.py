@@ -130,3 +130,34 @@ def test_gemv_beyond_2gib_of_weights(q4, orc):
         close(got, orc.q4_gemv(x.numpy(), qs_o, sm_o, K), "gemv %d x %d x %d (sampled rows)" % (M, N, K))
     del qs, sm
     torch.cuda.empty_cache()
+
+
+def test_gemv_g32_beyond_2gib_of_weights(q4, orc):
+    # the group-32 GEMV on 1048576 x 4096 weights: two row ranges (1048512
+    # rows and 64) as above, and at M >= 2 a K split in two whose partials
+    # for every range fit the workspace sized for the whole shape
+    N, K = 1048576, 4096
+    say("gemv g32 beyond 2 GiB of weights: N=%d K=%d" % (N, K))
+    g = torch.Generator(device="cuda").manual_seed(67)
+    W = torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32).mul_(0.02)
+    qs, sm = q4.q4_pack_g32(W)
+    boundary = 1048512
+    rows = np.unique(np.concatenate([[0, 1, boundary - 2, boundary - 1, boundary, boundary + 1, N - 2, N - 1],
+                                     np.random.default_rng(68).choice(N, 500, replace=False)]))
+    ridx = torch.from_numpy(rows).cuda()
+    Wr = W.index_select(0, ridx).cpu().numpy()
+    del W
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    qs_o, sm_o = orc.q4_pack(Wr, group=32)
+    assert np.array_equal(qs.index_select(0, ridx).cpu().numpy(), qs_o)
+    assert np.array_equal(sm.index_select(0, ridx).cpu().view(torch.int16).numpy().view(np.uint16), sm_o)
+    for M in (1, 2, 8, 16):
+        say("  M=%d (workspace %d bytes)" % (M, q4.q4_gemv_g32_workspace_bytes(M, N, K)))
+        x = wl.draw_activations(wl.generator(69 + M), M, K)
+        y = q4.q4_gemv_g32(dev(x), qs, sm)
+        got = y.index_select(1, ridx).cpu().numpy()
+        close(got, orc.q4_gemv(x.numpy(), qs_o, sm_o, K, group=32),
+              "gemv g32 %d x %d x %d (sampled rows)" % (M, N, K))
+    del qs, sm
+    torch.cuda.empty_cache()
