@@ -271,14 +271,16 @@ int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *
  * of 256 on top of Q8_1's own rounding; results match the fp64 definition to
  * max|dy| / max|y| <= 2e-3 and NMSE <= 1e-6 (measured NMSE ~3e-8 on N(0,1)
  * activations with outliers up to 1000x).  Reruns are bit-identical.
- * Grids of at least 256 tiles of 128 x 128 run a pipelined kernel whose prep
+ * Grids of at least 256 tiles of 128 x 128 whose activations, packed weights
+ * and records each stay below 2 GiB run a pipelined kernel whose prep
  * pass writes, per (activation row, group), the block scales D, step, X and
  * the centring term 8 * sum_b D * sum_{k in b} a, and per (weight row, group)
  * scale and minimum + 8 scale in fp32, into the workspace (32 bytes per
  * activation row and 8 bytes per weight row, per group, rows rounded up to
- * 128).  Smaller grids split K over workgroups into fp32 partials in the
- * workspace, summed in split order by a second kernel (no workspace when K
- * is not split).
+ * 128).  Other shapes run an unpipelined kernel over row ranges of less
+ * than 2 GiB of each operand; small grids split K over workgroups into fp32
+ * partials in the workspace, summed in split order by a second kernel (no
+ * workspace when K is not split).
  *   Arguments, layouts and errors as q4_mmq_gemm; workspace: at least
  *   q4_mmq_int8_workspace_bytes(M, N, K) bytes (pure host function, 0 for
  *   shapes the call would reject).
