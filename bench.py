@@ -61,10 +61,22 @@ def mmq_bytes(M, N, K):
     return N * K // 2 + N * (K // 256) * 4 + M * K + M * (K // 32) * 4 + M * N * 4
 
 
+def f16_tile_rows(M, N):
+    """Activation rows per tile of the fp16 design: 192 where the grid of
+    256-row tiles fills at most two rounds of 256 CUs and 192-row tiles take
+    fewer rows x rounds, else 256."""
+    nt = (N + 127) // 128
+    t256, t192 = (M + 255) // 256 * nt, (M + 191) // 192 * nt
+    if t256 > 512:
+        return 256
+    return 192 if (t192 + 255) // 256 * 192 < (t256 + 255) // 256 * 256 else 256
+
+
 def f16_workspace_bytes(M, N, K):
-    """Workspace of q4_mmq_gemm's fp16 design: the fp16 activation image, row
-    factors and the weight rows' exponents."""
-    rows = (M + 255) // 256 * 256
+    """Workspace of q4_mmq_gemm's fp16 design: the fp16 activation image (rows
+    padded to whole tiles), row factors and the weight rows' exponents."""
+    fm = f16_tile_rows(M, N)
+    rows = (M + fm - 1) // fm * fm
     return rows * K * 2 + rows * 4 + (N + 127) // 128 * 128 * 8
 
 

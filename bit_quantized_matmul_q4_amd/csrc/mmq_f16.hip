@@ -38,6 +38,11 @@
 //     four masks, and the prep pass writes the activations in that order.
 //   * Tile 256 (m) x 128 (n), 512 threads = 8 waves, two per SIMD: one wave
 //     per SIMD loads, one computes 128 x 64 outputs (4 x 2 MFMA tiles).
+//     Grids whose 256-row tiles would leave CUs idle in their last round
+//     (at most two rounds) take 192-row tiles where that means fewer rows x
+//     rounds (96 x 64 per computing wave): M 512 at N 9216 runs 216 tiles
+//     of 192 rows in one round instead of 144 of 256.  The arithmetic is
+//     the same per output, so the results are identical bit for bit.
 //   * Each K step (32 KB of image, 4 KB of packed weights) is loaded straight
 //     into one of 4 LDS stages (no registers in flight, two steps ahead);
 //     the computing waves read and unpack each MFMA round's operands during
@@ -57,29 +62,35 @@ namespace q4mi {
 
 namespace {
 
-constexpr int kFm = 256;           // activation rows per tile
+// activation rows per tile: 256, or 192 where the grid of 256-row tiles
+// leaves CUs idle in its last round (the launcher's choice, tile_rows)
+constexpr int kFm = 256;
+constexpr int kFmSmall = 192;
 constexpr int kFn = 128;           // weight rows per tile
 constexpr int kFk = 64;            // K per step: two Q8_1 blocks
-constexpr int kFThreads = 256;
 // K steps per image workgroup: two (128 B of a row per thread, whole cache
 // lines) while that still leaves kImgMinGroups workgroups, else one
 constexpr int kImgMaxSteps = 2;
 constexpr int kImgMinGroups = 256;
 static_assert(kGroup % (kFk * kImgMaxSteps) == 0, "K (a multiple of 256) holds whole image workgroups");
-constexpr int kStepVecs = 8 * kFm; // 16-byte vectors of the image per (tile, step)
+// 16-byte vectors of the image per (tile of fm rows, step)
+__host__ __device__ constexpr int step_vecs(int fm) { return 8 * fm; }
 // Computing waves (one per SIMD) and the 32-row activation tiles each owns.
 // Eight computing waves (two per SIMD, 64 x 64 each, 129 registers) were
 // 3-6 % slower at M 512-2048: each weight tile's fragments are then read and
 // unpacked by four waves instead of two.
 constexpr int kCW = 4;
-constexpr int kTI = kFm / 32 / (kCW / 2);
 constexpr int kGemmThreads = (kCW + 4) * kWave;  // and one loading wave per SIMD
 constexpr int kStages = 4;                      // K steps in LDS at once
-constexpr int kStageVecs = kStepVecs + 2 * kFn; // image + packed weights of a step
 constexpr int kSmVecs32 = 2 * kFn / 4;          // group 32: the step's (scale, minimum) pairs
-// 144 KB of stages; with group-32 weights 148 KB
-__host__ __device__ constexpr int stage_vecs(bool g32) { return kStageVecs + (g32 ? kSmVecs32 : 0); }
-static_assert(kStages * stage_vecs(true) * 16 + 3 * kFn * 4 + kFn * 8 <= 160 * 1024, "LDS of a CU");
+// image + packed weights of a step (+ group-32 pairs): 144 KB of stages at
+// 256 rows, 148 KB with group-32 weights
+__host__ __device__ constexpr int stage_vecs(int fm, bool g32)
+{
+    return step_vecs(fm) + 2 * kFn + (g32 ? kSmVecs32 : 0);
+}
+static_assert(kStages * stage_vecs(kFm, true) * 16 + 3 * kFn * 4 + kFn * 8 <= 160 * 1024, "LDS of a CU");
+static_assert(kFmSmall % 64 == 0 && kFmSmall < kFm, "whole 32-row MFMA tiles per computing wave");
 // largest activation image per launch; bigger M runs in row chunks
 constexpr int64_t kImageMaxBytes = (int64_t)256 << 20;
 
@@ -150,17 +161,18 @@ __device__ __forceinline__ int weight_exponent(float wmax)
 // weight row's exponent E (weight_exponent over its P pairs) for rows [0,
 // Np), Np = N rounded up to whole 128-row tiles: wexp[n] = (E, 2^-E as fp32
 // bits), (0, 1.0) past N.
-template <bool kRowScale, int kSteps>
-__global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restrict__ qa,
+template <bool kRowScale, int kSteps, int FM>
+__global__ __launch_bounds__(kFm) void k_mmqf_image(const int8_t *__restrict__ qa,
                                                           const uint32_t *__restrict__ ds,
                                                           float *__restrict__ fs, int M, int K,
                                                           uint4 *__restrict__ img,
                                                           const uint32_t *__restrict__ sm, int N, int P,
                                                           int Np, int2 *__restrict__ wexp)
 {
+    constexpr int kFm = FM, kStepVecs = step_vecs(FM);
     if ((int)blockIdx.y == (int)gridDim.y - 1) {
-        const int stride = (int)gridDim.x * kFThreads;
-        for (int n = (int)blockIdx.x * kFThreads + (int)threadIdx.x; n < Np; n += stride) {
+        const int stride = (int)gridDim.x * FM;
+        for (int n = (int)blockIdx.x * FM + (int)threadIdx.x; n < Np; n += stride) {
             float wmax = 0.0f;
             if (n < N) {
                 // eight loads in flight at a time
@@ -253,14 +265,18 @@ __global__ __launch_bounds__(kFThreads) void k_mmqf_image(const int8_t *__restri
 // form one stream: the loading waves run into the next tile's steps while
 // the computing waves write the last tile's outputs, whose stores drain
 // while the next tile computes.
-template <int kMode, bool kG32 = false>
+template <int kMode, bool kG32, int FM>
 __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     const uint4 *__restrict__ img, uint32_t img_bytes, const float *__restrict__ fs,
     const uint8_t *__restrict__ qs, const uint32_t *__restrict__ sm, const int2 *__restrict__ wexp,
     float *__restrict__ y, int8_t *__restrict__ qo, uint32_t *__restrict__ dso, int M, int N, int K,
     int tiles_m, int ntiles, int64_t ldy, int vec_store)
 {
-    constexpr int kSV = stage_vecs(kG32);
+    // tile of FM activation rows: kTI 32-row MFMA tiles per computing wave,
+    // kIP image pieces of 64 vectors per loading wave and step
+    constexpr int kFm = FM, kStepVecs = step_vecs(FM), kTI = FM / 32 / (kCW / 2), kIP = FM / 32;
+    constexpr int kStageVecs = step_vecs(FM) + 2 * kFn;
+    constexpr int kSV = stage_vecs(FM, kG32);
     __shared__ int4_t lds[kStages * kSV];
     __shared__ uint32_t sSM[2][kFn];
     __shared__ int2 sWE[2][kFn];  // (E, 2^-E) of the weight rows of tiles with even / odd index
@@ -296,9 +312,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
     const uint32_t we0 = lds_addr(&sWE[0][0]);
 
     if (!consumer) {
-        // ---- producer: step u in stage u % kStages; 8 image pieces (2048
+        // ---- producer: step u in stage u % kStages; kIP image pieces (8 FM
         // vectors / 4 producers), one weight piece, with group-32 weights one
-        // piece of pairs: at least 9 loads per step.  Barrier B_u (the
+        // piece of pairs: at least kIP + 1 loads per step.  Barrier B_u (the
         // consumers' barrier between rounds 2 and 3 of step u) needs step
         // u + 1 in LDS; after it, step u + kStages - 1 goes into the stage of
         // step u - 1, whose reads the consumers finished before B_u.  Steps
@@ -311,8 +327,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
             const uint32_t stage = lds0 + (uint32_t)((u % kStages) * kSV) * 16u;
             const uint32_t goff = (uint32_t)((mt * S + sl) * kStepVecs) * 16u;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t v = (uint32_t)(pw * 512 + i * 64);
+            for (int i = 0; i < kIP; ++i) {
+                const uint32_t v = (uint32_t)(pw * kIP * 64 + i * 64);
                 dma16(r_img, (v + lane) * 16u, goff, stage + v * 16u);
             }
             dma16(r_qs, ((uint32_t)n0 + wcol) * rowq + wblk * 16u, (uint32_t)sl * 32u,
@@ -340,10 +356,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_mmqf(
         issue_we(0);
         issue_sm(0);
         for (int u = 0; u < kStages - 2; ++u) issue(u);
-        wait_vm_barrier<9 * (kStages - 3)>();  // B_init: step 0, its pairs and exponents
+        wait_vm_barrier<(kIP + 1) * (kStages - 3)>();  // B_init: step 0, its pairs and exponents
         issue(kStages - 2);
         for (int u = 0; u < U; ++u) {
-            wait_vm_barrier<9 * (kStages - 3)>();  // B_u: step u + 1
+            wait_vm_barrier<(kIP + 1) * (kStages - 3)>();  // B_u: step u + 1
             issue(u + kStages - 1);
             if ((u & 3) == 0) issue_sm((u >> 2) + 1);
             // from B_{k S} on the consumers are past tile k - 1's epilogue,
@@ -560,15 +576,35 @@ int64_t round_up(int64_t v, int64_t u) { return (v + u - 1) / u * u; }
 
 constexpr int64_t kFusedScaleBytes = (int64_t)8 << 20;
 
-// activation rows per launch: the whole (padded) M, or as many 256-row tiles
-// as keep the image within kImageMaxBytes (at least one tile)
-int64_t chunk_rows(int64_t M, int64_t K)
+// Activation rows per tile, from the shape alone (the workspace size follows
+// it): 192 where the grid of 256-row tiles fills at most two rounds of the
+// CUs and 192-row tiles take fewer rows x rounds, e.g. M 512 at N 9216 (144
+// tiles of 256 rows on 256 CUs, 216 of 192 rows: one round either way);
+// otherwise 256.
+int tile_rows(int64_t M, int64_t N)
 {
-    int64_t per = (kImageMaxBytes / (2 * K)) / kFm * kFm;
-    if (per < kFm) per = kFm;
-    const int64_t mp = round_up(M, kFm);
+    constexpr int64_t kCus = 256;
+    const int64_t nt = (N + kFn - 1) / kFn;
+    const int64_t t256 = (M + kFm - 1) / kFm * nt, t192 = (M + kFmSmall - 1) / kFmSmall * nt;
+    if (t256 > 2 * kCus) return kFm;
+    const int64_t c256 = (t256 + kCus - 1) / kCus * kFm, c192 = (t192 + kCus - 1) / kCus * kFmSmall;
+    return c192 < c256 ? kFmSmall : kFm;
+}
+
+// activation rows per launch: the whole (padded) M, or as many fm-row tiles
+// as keep the image within kImageMaxBytes (at least one tile)
+int64_t chunk_rows(int64_t M, int64_t K, int fm)
+{
+    int64_t per = (kImageMaxBytes / (2 * K)) / fm * fm;
+    if (per < fm) per = fm;
+    const int64_t mp = round_up(M, fm);
     return mp < per ? mp : per;
 }
+
+template <int FM>
+hipError_t launch_mmqf_t(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                         const uint16_t *sm, int64_t N, int K, bool g32, float *y, int8_t *qo, uint16_t *dso,
+                         void *workspace, int num_cus, hipStream_t stream);
 
 }  // namespace
 
@@ -577,7 +613,7 @@ int64_t chunk_rows(int64_t M, int64_t K)
 size_t mmqf_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < kGroup) return 0;
-    const int64_t rows = chunk_rows(M, K);
+    const int64_t rows = chunk_rows(M, K, tile_rows(M, N));
     return (size_t)(rows * K * 2 + rows * (int64_t)sizeof(float) + round_up(N, kFn) * (int64_t)sizeof(int2));
 }
 
@@ -585,10 +621,23 @@ hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const ui
                        const uint16_t *sm, int64_t N, int K, bool g32, float *y, int8_t *qo, uint16_t *dso,
                        void *workspace, int num_cus, hipStream_t stream)
 {
+    if (tile_rows(M, N) == kFmSmall)
+        return launch_mmqf_t<kFmSmall>(qa, ds, M, qs, sm, N, K, g32, y, qo, dso, workspace, num_cus, stream);
+    return launch_mmqf_t<kFm>(qa, ds, M, qs, sm, N, K, g32, y, qo, dso, workspace, num_cus, stream);
+}
+
+namespace {
+
+template <int FM>
+hipError_t launch_mmqf_t(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *qs,
+                         const uint16_t *sm, int64_t N, int K, bool g32, float *y, int8_t *qo, uint16_t *dso,
+                         void *workspace, int num_cus, hipStream_t stream)
+{
+    constexpr int kFm = FM;
     const int B = K / kBlock, S = K / kFk;
     const int P = g32 ? B : K / kGroup;  // (scale, minimum) pairs per weight row
     if (g32 && !y) return hipErrorInvalidValue;  // group 32: fp32 output only
-    const int64_t rows_max = chunk_rows(M, K);
+    const int64_t rows_max = chunk_rows(M, K, FM);
     const int64_t npad = round_up(N, kFn);
     if (npad > 0x7FFFFFFF) return hipErrorInvalidValue;
     uint4 *img = static_cast<uint4 *>(workspace);
@@ -611,14 +660,14 @@ hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const ui
         const bool two = (int64_t)(S / kImgMaxSteps) * tiles_m >= kImgMinGroups;
         const dim3 igrid((unsigned)(two ? S / kImgMaxSteps : S), (unsigned)(tiles_m + 1));
         if (mp * S * B * 4 <= kFusedScaleBytes && (reinterpret_cast<uintptr_t>(ds) & 15) == 0) {
-            auto kimg = two ? k_mmqf_image<true, kImgMaxSteps> : k_mmqf_image<true, 1>;
-            hipLaunchKernelGGL(kimg, igrid, dim3(kFThreads), 0, stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm,
+            auto kimg = two ? k_mmqf_image<true, kImgMaxSteps, FM> : k_mmqf_image<true, 1, FM>;
+            hipLaunchKernelGGL(kimg, igrid, dim3(FM), 0, stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm,
                                K, img, sm32, (int)N, P, (int)npad, wexp);
         } else {
             hipLaunchKernelGGL(k_mmqf_rowscale, dim3((unsigned)(mp / 4)), dim3(256), 0, stream, ds32 + m0 * B,
                                (int)mm, B, (int)mp, fs);
-            auto kimg = two ? k_mmqf_image<false, kImgMaxSteps> : k_mmqf_image<false, 1>;
-            hipLaunchKernelGGL(kimg, igrid, dim3(kFThreads), 0, stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm,
+            auto kimg = two ? k_mmqf_image<false, kImgMaxSteps, FM> : k_mmqf_image<false, 1, FM>;
+            hipLaunchKernelGGL(kimg, igrid, dim3(FM), 0, stream, qa + m0 * K, ds32 + m0 * B, fs, (int)mm,
                                K, img, sm32, (int)N, P, (int)npad, wexp);
         }
         for (int64_t n0 = 0; n0 < N; n0 += n_max) {
@@ -632,12 +681,12 @@ hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const ui
                 float *y0 = y + m0 * N + n0;
                 const int vec_store = (N % 4 == 0) && (nn % 4 == 0) &&
                                       ((reinterpret_cast<uintptr_t>(y0) & 15) == 0);
-                auto kern = g32 ? k_mmqf<kFOutY, true> : k_mmqf<kFOutY, false>;
+                auto kern = g32 ? k_mmqf<kFOutY, true, FM> : k_mmqf<kFOutY, false, FM>;
                 hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), 0, stream, img, img_bytes, fs,
                                    qs + n0 * (K / 2), sm32 + n0 * P, wexp + n0, y0, (int8_t *)nullptr,
                                    (uint32_t *)nullptr, (int)mm, (int)nn, K, tiles_m, (int)tiles, N, vec_store);
             } else {
-                hipLaunchKernelGGL((k_mmqf<kFOutQ8, false>), dim3(grid), dim3(kGemmThreads), 0, stream, img,
+                hipLaunchKernelGGL((k_mmqf<kFOutQ8, false, FM>), dim3(grid), dim3(kGemmThreads), 0, stream, img,
                                    img_bytes, fs, qs + n0 * (K / 2), sm32 + n0 * P, wexp + n0, (float *)nullptr,
                                    qo + m0 * N + n0, dso32 + m0 * (N / kBlock) + n0 / kBlock, (int)mm, (int)nn, K,
                                    tiles_m, (int)tiles, N, 0);
@@ -648,5 +697,7 @@ hipError_t launch_mmqf(const int8_t *qa, const uint16_t *ds, int64_t M, const ui
     }
     return hipSuccess;
 }
+
+}  // namespace
 
 }  // namespace q4mi

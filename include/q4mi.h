@@ -202,8 +202,9 @@ int q4_mmq_gemm_g32(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8
 /*
  * q4_mmq_workspace_bytes -- device workspace q4_mmq_gemm (and
  * q4_mmq_gemm_q8_1, q4_mmq_gemm_g32) needs for this shape: the fp16
- * activation image of the fp16 path (2 * K bytes per activation row, at
- * most 256 MiB + 2 * K * 256 bytes, plus 4 bytes per row) and 8 bytes per
+ * activation image of the fp16 path (2 * K bytes per activation row, rows
+ * padded to whole tiles of 256 or 192, at most 256 MiB + 2 * K * 256
+ * bytes, plus 4 bytes per row) and 8 bytes per
  * weight row (N rounded up to 128), or what the int8 path needs
  * (q4_mmq_int8_workspace_bytes).  Pure host function.  Returns 0
  * for shapes q4_mmq_gemm would reject.
@@ -221,7 +222,9 @@ size_t q4_mmq_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *     CU evenly busy (at least 128 tiles, and at most 256 or rounds of 256
  *     at least 80 % full; e.g. M = 2048 at N = 4096 or 12288, M = 512 at
  *     N = 9216), unless the int8 design's 128 x 128 tiles fill the CUs in
- *     one round (at most 256 tiles; e.g. M = 1024 at N = 4096): a prep pass
+ *     one round (at most 256 tiles; e.g. M = 1024 at N = 4096), with
+ *     192-row tiles where those fill the CUs better (e.g. M = 512 at
+ *     N = 9216; the result is the same bit for bit): a prep pass
  *     writes each activation as fp16(d * a * 2^f[m]),
  *     one power of two per row so that the largest is below 2^15; the GEMM
  *     turns each weight into fp16((scale * q + minimum) * 2^e[n]) in one

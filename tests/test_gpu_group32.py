@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from bit_quantized_matmul_q4_amd import workloads as wl
-from test_gpu_parity import MAX_NMSE, MAX_REL, close, dev, say  # noqa: F401
+from test_gpu_parity import MAX_NMSE, MAX_REL, close, dev, f16_workspace, say  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -163,7 +163,7 @@ def test_mmq_g32_equal_pairs_match_g256(q4, orc):
 def test_mmq_g32_f16_ragged(q4, orc):
     M, N, K = 300, 12700, 512
     say("mmq g32, fp16 design, M=%d N=%d K=%d" % (M, N, K))
-    assert q4.q4_mmq_workspace_bytes(M, N, K) == (M + 255) // 256 * 256 * (2 * K + 4) + (N + 127) // 128 * 128 * 8
+    assert q4.q4_mmq_workspace_bytes(M, N, K) == f16_workspace(M, N, K)  # two tiles of 192 rows
     mmq_g32_check(q4, orc, M, N, K, 74, True, "mmq g32 fp16 ragged")
 
 

@@ -597,13 +597,25 @@ def test_mmq_degenerate_groups(q4, orc):
 
 # ------------------------------------------------- MMQ, fp16 matrix cores ---
 # Shapes whose grid of 256 x 128 tiles fills the GPU run on the fp16 design;
-# its workspace (the fp16 activation image, 2 K bytes per row padded to 256
-# rows, plus 4 bytes per row) tells which design a shape takes.
+# its workspace (the fp16 activation image, 2 K bytes per row padded to whole
+# tiles of 256 or 192 rows, plus 4 bytes per row) tells which design a shape
+# takes.
+
+def f16_tile_rows(M, N):
+    # 192-row tiles where the grid of 256-row tiles fills at most two rounds
+    # of 256 CUs and 192-row tiles take fewer rows x rounds, else 256
+    nt = (N + 127) // 128
+    t256, t192 = (M + 255) // 256 * nt, (M + 191) // 192 * nt
+    if t256 > 512:
+        return 256
+    return 192 if (t192 + 255) // 256 * 192 < (t256 + 255) // 256 * 256 else 256
+
 
 def f16_workspace(M, N, K):
-    # activation image (2 K bytes per row, rows padded to 256), a row factor
-    # per row, and (E, 2^-E) per weight row (rows padded to 128)
-    rows = (M + 255) // 256 * 256
+    # activation image (2 K bytes per row, rows padded to whole tiles), a row
+    # factor per row, and (E, 2^-E) per weight row (rows padded to 128)
+    fm = f16_tile_rows(M, N)
+    rows = (M + fm - 1) // fm * fm
     return rows * K * 2 + rows * 4 + (N + 127) // 128 * 128 * 8
 
 
