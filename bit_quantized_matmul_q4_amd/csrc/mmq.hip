@@ -609,10 +609,16 @@ bool mmq_uses_f16(int64_t M, int64_t N, int64_t K)
 // The int8 design's fp32-output kernels: the pipelined k_mmqi (mmq_i8.hip,
 // 128 x 128 tiles, one workgroup per CU) when its grid has at least one tile
 // per CU, otherwise k_mmq here (128 x 128 tiles, two per CU, K split for
-// small grids).  A function of the shape only.
+// small grids).  Grids of more than one but less than two rounds of k_mmqi
+// (257 to 511 tiles) also take k_mmq, which runs them in one round (M 512,
+// 2560 -> 9216, 288 tiles: 62.5 -> 60.0 us; 384 tiles: the same time; the
+// same integer sums, bit-identical).  A function of the shape only.
 bool mmq_int8_pipelined(int64_t M, int64_t N, int64_t K)
 {
+    constexpr int64_t kCus = 256;
     const int64_t tiles = ((M + 255) / 256) * ((N + 127) / 128);
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    if (t128 > kCus && t128 < 2 * kCus) return false;
     return tiles >= 128 && mmqi_supported(M, N, K);
 }
 

@@ -274,7 +274,8 @@ int q4_mmq_gemm(const int8_t *qa, const uint16_t *ds, int64_t M, const uint8_t *
  * of 256 on top of Q8_1's own rounding; results match the fp64 definition to
  * max|dy| / max|y| <= 2e-3 and NMSE <= 1e-6 (measured NMSE ~3e-8 on N(0,1)
  * activations with outliers up to 1000x).  Reruns are bit-identical.
- * Grids of at least 256 tiles of 128 x 128 whose activations, packed weights
+ * Grids of at least 256 tiles of 128 x 128 (but not 257 to 511, which the
+ * unpipelined kernel runs in one round) whose activations, packed weights
  * and records each stay below 2 GiB run a pipelined kernel whose prep
  * pass writes, per (activation row, group), the block scales D, step, X and
  * the centring term 8 * sum_b D * sum_{k in b} a, and per (weight row, group)

@@ -54,7 +54,10 @@ def test_graph_replays_match_eager(q4):
     dsf5 = torch.empty((512, 128, 2), dtype=torch.float16, device=dev)
     yf = torch.empty((300, 12288), device=dev)
     yf5 = torch.empty((512, 9216), device=dev)
-    yi5 = torch.empty((512, 9216), device=dev)
+    xi5 = torch.empty((1024, 4096), device=dev)
+    qai5 = torch.empty((1024, 4096), dtype=torch.int8, device=dev)
+    dsi5 = torch.empty((1024, 128, 2), dtype=torch.float16, device=dev)
+    yi5 = torch.empty((1024, 9216), device=dev)
     qof = torch.empty((300, 12288), dtype=torch.int8, device=dev)
     dsof = torch.empty((300, 384, 2), dtype=torch.float16, device=dev)
     yg1 = torch.empty((1, 6144), device=dev)
@@ -64,22 +67,23 @@ def test_graph_replays_match_eager(q4):
     qs3g, sm3g = q4.q4_pack_g32(w(224, 2048))
     ws_f = torch.empty((q4.q4_mmq_workspace_bytes(300, 12288, 512),), dtype=torch.uint8, device=dev)
     ws_f5 = torch.empty((q4.q4_mmq_workspace_bytes(512, 9216, 4096),), dtype=torch.uint8, device=dev)
-    ws_i5 = torch.empty((max(q4.q4_mmq_int8_workspace_bytes(512, 9216, 4096), 1),), dtype=torch.uint8, device=dev)
+    ws_i5 = torch.empty((max(q4.q4_mmq_int8_workspace_bytes(1024, 9216, 4096), 1),), dtype=torch.uint8, device=dev)
     ws_g8 = torch.empty((max(q4.q4_gemv_g32_workspace_bytes(8, 6144, 2560), 1),), dtype=torch.uint8, device=dev)
     # the fp16 design's workspace holds its activation image (2 K bytes per
-    # row, rows padded to 256, plus 4 bytes per row) and 8 bytes per weight
-    # row, and covers the K-split partials of the Q8_1-output and group-32
-    # int8 kernels where those exceed it; q4_mmq_gemm_int8 has its own (the
-    # per-row and per-weight-row records of its pipelined kernel)
+    # row, rows padded to whole tiles, plus 4 bytes per row) and 8 bytes per
+    # weight row, and covers the K-split partials of the Q8_1-output and
+    # group-32 int8 kernels where those exceed it; q4_mmq_gemm_int8 has its
+    # own (the per-row and per-weight-row records of its pipelined kernel,
+    # which 576 tiles of 128 x 128 take)
     assert q4.q4_mmq_workspace_bytes(300, 12288, 512) == 384 * (2 * 512 + 4) + 12288 * 8  # two 192-row tiles
     assert q4.q4_mmq_workspace_bytes(512, 9216, 4096) == 576 * (2 * 4096 + 4) + 9216 * 8  # three 192-row tiles
-    assert q4.q4_mmq_int8_workspace_bytes(512, 9216, 4096) == 512 * 16 * 32 + 9216 * 16 * 8
+    assert q4.q4_mmq_int8_workspace_bytes(1024, 9216, 4096) == 1024 * 16 * 32 + 9216 * 16 * 8
     # the shapes take the K-split paths (partials and a second, summing kernel)
     assert q4.q4_mmq_workspace_bytes(100, 224, 2048) > 0
     assert q4.q4_gemv_workspace_bytes(8, 512, 4096) > 0
 
     def inputs():
-        for t in (xa, x1, x2, x8, x8g, xf, xf5):
+        for t in (xa, x1, x2, x8, x8g, xf, xf5, xi5):
             t.copy_(torch.randn(t.shape, generator=g, device=dev))
 
     def run():
@@ -94,13 +98,14 @@ def test_graph_replays_match_eager(q4):
         q4.q4_mmq_gemm_q8_1(qaf, dsf, qs4, sm4, qa_out=qof, ds_out=dsof, workspace=ws_f)
         q4.q8_1_quantize(xf5, qaf5, dsf5)
         q4.q4_mmq_gemm(qaf5, dsf5, qs5, sm5, y=yf5, workspace=ws_f5)
-        q4.q4_mmq_gemm_int8(qaf5, dsf5, qs5, sm5, y=yi5, workspace=ws_i5)
+        q4.q8_1_quantize(xi5, qai5, dsi5)
+        q4.q4_mmq_gemm_int8(qai5, dsi5, qs5, sm5, y=yi5, workspace=ws_i5)
         q4.q4_gemv_g32(x1, g1, gs1, y=yg1)
         q4.q4_gemv_g32(x8g, g1, gs1, y=yg8, workspace=ws_g8)
         q4.q4_mmq_gemm_g32(qa, ds, qs3g, sm3g, y=ygm, workspace=ws_m)
         q4.q4_mmq_gemm_g32(qaf, dsf, g4, gs4, y=ygf, workspace=ws_f)
 
-    outs = (qa, ds, ym, qo, dso, y1, y2, y8, qaf, dsf, yf, qof, dsof, qaf5, dsf5, yf5, yi5, yg1, yg8, ygm, ygf)
+    outs = (qa, ds, ym, qo, dso, y1, y2, y8, qaf, dsf, yf, qof, dsof, qaf5, dsf5, yf5, qai5, dsi5, yi5, yg1, yg8, ygm, ygf)
     inputs()
     run()  # warm: per-device state is set up outside the capture
     torch.cuda.synchronize()
